@@ -1,0 +1,133 @@
+/*
+ * s2attn.h -- C ABI of the MI355X (gfx950) shifted sparse attention engine.
+ *
+ * Shifted sparse attention (S²-Attn) as described on the PaperTrace page
+ * "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调" (§1 "S²-Attn的计算图") and in
+ * the study notes "精读笔记：LongLoRA" (§3.2): the sequence is cut into groups
+ * of G tokens and each group runs causal attention on its own.  Heads
+ * [0, H/2) group on the original boundaries; heads [H/2, H) group after a
+ * shift of s = G/2 tokens and their outputs land back on the original
+ * positions.  Two boundary variants of the shifted heads exist:
+ *
+ *   S2A_WRAP  -- the original roll: the rolled layout is cut into N/G
+ *                groups, so the last group holds positions
+ *                [N-s .. N-1, 0 .. s-1] with the causal triangle taken in
+ *                that order (queries 0..s-1 read keys N-s..N-1);
+ *   S2A_SPLIT -- the strict-causal variant: groups [0, s), [s+kG, s+(k+1)G)
+ *                for k = 0..N/G-2, and [N-s, N).
+ *
+ * Both come from §1's paragraph on cyclic shifts (Figure 1, right and left).
+ * A padded tail is masked inside every softmax: keys at positions >= the
+ * valid length never contribute (§1, paragraph on padding to whole groups).
+ * If N/G == 1 the shift has no effect (both head classes are plain causal
+ * attention over the whole sequence).
+ *
+ * Layouts (all tensors dense, row-major, on the device):
+ *   q, k, v, dout      bf16  [B, N, H, D]   N = padded length
+ *   o                  bf16 or f32 [B, N, H, D]
+ *   lse, delta         f32   [B, H, N]      natural log-sum-exp of the
+ *                                           scaled logits of each row
+ *   dq, dk, dv         f32   [B, N, H, D]
+ *   gid, slot, src     int32 [2, N]         index maps, class 0 then 1
+ *
+ * Ownership and streams: the caller owns every buffer.  The library never
+ * allocates, frees or synchronises; work is enqueued on `stream` (a
+ * hipStream_t; NULL = the null stream) and is complete when that stream
+ * reaches it.  Inputs must not alias outputs.
+ *
+ * Errors: every argument is checked before anything is enqueued; on an
+ * error nothing is written and nothing is launched.  Status codes are
+ * returned, never thrown; s2attn_last_error() gives a thread-local
+ * description of the last failure on the calling thread.
+ */
+#ifndef S2ATTN_H
+#define S2ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  S2A_OK = 0,
+  S2A_EINVAL = 1,       /* bad size, shift, valid length, pointer, scale */
+  S2A_EUNSUPPORTED = 2, /* head width D not in {16, 32, 64, 128}          */
+  S2A_EHIP = 3          /* a HIP launch failed                            */
+} s2a_status;
+
+typedef enum { S2A_WRAP = 0, S2A_SPLIT = 1 } s2a_boundary;
+typedef enum { S2A_BF16 = 0, S2A_F32 = 1 } s2a_dtype;
+
+/*
+ * Forward.  For every head h, group and query x < valid_len with visible
+ * set S_x (same group, at or before x in group order, key position <
+ * valid_len):
+ *   o[x]   = sum_{y in S_x} softmax_y(scale * q[x].k[y]) v[y]
+ *   lse[x] = ln sum_{y in S_x} exp(scale * q[x].k[y])
+ * (PaperTrace LongLoRA §3, the equation for o_i^s; the per-row
+ * log-sum-exp of §1.1 is kept in place of the probabilities).
+ * Rows x >= valid_len get o = 0 and lse = -inf.
+ *
+ * Arguments: q, k, v bf16 [B,N,H,D]; o of dtype o_dtype [B,N,H,D];
+ * lse f32 [B,H,N]; N the padded length; shift 0 (plain grouping) or G/2;
+ * valid_len in [1, N]; scale > 0 and finite (1/sqrt(D) in the method).
+ * Checks (PaperTrace LongLoRA §1, launch-time asserts): H % 2 == 0,
+ * G % 2 == 0, N % G == 0, all sizes > 0, pointers non-NULL and 16-byte
+ * aligned.  Returns S2A_EINVAL / S2A_EUNSUPPORTED / S2A_EHIP / S2A_OK.
+ */
+s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
+                      int o_dtype, float *lse, int B, int N, int H, int D,
+                      int G, int shift, int boundary, int valid_len,
+                      float scale, void *stream);
+
+/*
+ * Backward.  Given dout = dL/do and the o, lse produced by s2attn_fwd with
+ * the same arguments, writes (overwriting) the gradients of L:
+ *   a_xy  = exp(scale * q[x].k[y] - lse[x]),  delta_x = dout[x].o[x]
+ *   dz_xy = a_xy * (dout[x].v[y] - delta_x)
+ *   dq[x] = scale * sum_y dz_xy k[y],  dk[y] = scale * sum_x dz_xy q[x],
+ *   dv[y] = sum_x a_xy dout[x]
+ * summed over allowed pairs only (PaperTrace LongLoRA §3, the gradient of a
+ * logit; §1.1, the backward stays inside the groups).  Rows >= valid_len
+ * of dq, dk and dv are exactly 0.
+ *
+ * delta_ws: caller-provided f32 workspace of B*H*N floats; on return it
+ * holds delta_x.  dq is accumulated with device atomics, so its last bits
+ * may differ between runs; dk and dv are deterministic.
+ */
+s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
+                      const void *o, int o_dtype, const float *lse,
+                      const void *dout, float *dq, float *dk, float *dv,
+                      float *delta_ws, int B, int N, int H, int D, int G,
+                      int shift, int boundary, int valid_len, float scale,
+                      void *stream);
+
+/*
+ * Group index maps, computed on the device by the same group geometry the
+ * attention kernels use.  For head class c (0: heads < H/2, 1: the rest)
+ * and original position x:
+ *   gid[c*N + x]  = group of x,   slot[c*N + x] = rank of x in its group,
+ * and for row r of the regrouped layout (groups laid end to end in order):
+ *   src[c*N + r]  = original position held at row r.
+ * Class 0 groups are [kG, (k+1)G).  Class 1 follows `boundary` (WRAP:
+ * N/G groups of the layout rolled left by s; SPLIT: N/G + 1 groups, the
+ * first and last of length s).  The maps do not depend on valid_len (pad
+ * first, then shift), which is only validated.
+ */
+s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
+                            int valid_len, int *gid, int *slot, int *src,
+                            void *stream);
+
+/* Static description of a status code. */
+const char *s2attn_strerror(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *s2attn_last_error(void);
+
+/* Library version string. */
+const char *s2attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2ATTN_H */

@@ -1,0 +1,13 @@
+"""MI355X (gfx950) shifted sparse attention (S²-Attn) engine.
+
+The computation lives in libs2attn.so (hand-written HIP kernels behind the
+C ABI of include/s2attn.h).  This package only builds that library and
+marshals torch tensors into its calls.
+"""
+from . import _lib, work  # noqa: F401
+from ._lib import S2A_WRAP, S2A_SPLIT, S2AttnError, load  # noqa: F401
+from .ops import (fwd, bwd, group_map, s2_attention,  # noqa: F401
+                  S2AttnFunction)
+
+__all__ = ["fwd", "bwd", "group_map", "s2_attention", "S2AttnFunction",
+           "S2A_WRAP", "S2A_SPLIT", "S2AttnError", "load", "work"]

@@ -1,0 +1,164 @@
+// C ABI of the shifted sparse attention engine: argument checks, launch
+// geometry and error reporting.  See include/s2attn.h for the contract.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/s2attn.h"
+#include "s2a_device.h"
+#include "s2a_kernels.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+s2a_status fail(s2a_status st, const char *fmt, long long a = 0,
+                long long b = 0) {
+  snprintf(g_err, sizeof g_err, fmt, a, b);
+  return st;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Launch-time checks of the group shape: H % 2 == 0, G % 2 == 0 and
+// N % G == 0 after padding, the valid length inside [1, N], and only the
+// shifts 0 and G/2 (PaperTrace "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调",
+// §1, paragraph on asserting the divisibility conditions at launch).
+s2a_status check_shape(int B, int N, int H, int D, int G, int shift,
+                       int boundary, int valid_len) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0 || G <= 0)
+    return fail(S2A_EINVAL, "sizes must be positive");
+  if (H % 2) return fail(S2A_EINVAL, "H=%lld must be even", H);
+  if (G % 2) return fail(S2A_EINVAL, "G=%lld must be even", G);
+  if (N % G)
+    return fail(S2A_EINVAL, "padded N=%lld is not a multiple of G=%lld", N, G);
+  if (valid_len < 1 || valid_len > N)
+    return fail(S2A_EINVAL, "valid_len=%lld outside [1, N=%lld]", valid_len, N);
+  if (shift != 0 && shift != G / 2)
+    return fail(S2A_EINVAL, "shift=%lld must be 0 or G/2=%lld", shift, G / 2);
+  if (boundary != S2A_WRAP && boundary != S2A_SPLIT)
+    return fail(S2A_EINVAL, "boundary=%lld is neither WRAP nor SPLIT", boundary);
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(S2A_EUNSUPPORTED, "head width D=%lld not in {16,32,64,128}", D);
+  // Offsets of a row are formed in 64 bits; positions and grid sizes in 32.
+  const long long units = (long long)B * H * (N / G + 1);
+  if ((long long)B * N > (1ll << 31) || units * (G / 16 + 1) > (1ll << 31))
+    return fail(S2A_EINVAL, "problem too large for one launch");
+  return S2A_OK;
+}
+
+S2AGeom make_geom(int N, int G, int shift, int boundary, int L) {
+  S2AGeom g;
+  g.N = N;
+  g.G = G;
+  g.M = N / G;
+  g.s = (g.M == 1) ? 0 : shift;  // a single group has nothing to shift across
+  g.boundary = boundary;
+  g.L = L;
+  return g;
+}
+
+S2AParams make_params(int B, int N, int H, int G, int shift, int boundary,
+                      int L, float scale, int tile_rows) {
+  S2AParams p;
+  p.g = make_geom(N, G, shift, boundary, L);
+  p.B = B;
+  p.H = H;
+  p.ngmax = s2a_max_groups(p.g);
+  p.tiles = (G + tile_rows - 1) / tile_rows;
+  p.units = B * H * p.ngmax;
+  p.scale = scale;
+  p.scale_log2 = scale * S2A_LOG2E;
+  return p;
+}
+
+s2a_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return S2A_OK;
+  snprintf(g_err, sizeof g_err, "%s: %s", what, hipGetErrorString(e));
+  return S2A_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
+                      int o_dtype, float *lse, int B, int N, int H, int D,
+                      int G, int shift, int boundary, int valid_len,
+                      float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!q || !k || !v || !o || !lse)
+    return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
+    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
+                                  scale, s2a_fwd_tile_rows());
+  return hip_status(s2a_launch_fwd(q, k, v, o, o_dtype == S2A_F32, lse, D, p,
+                                   (hipStream_t)stream),
+                    "forward launch");
+}
+
+s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
+                      const void *o, int o_dtype, const float *lse,
+                      const void *dout, float *dq, float *dk, float *dv,
+                      float *delta_ws, int B, int N, int H, int D, int G,
+                      int shift, int boundary, int valid_len, float scale,
+                      void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws)
+    return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(delta_ws))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
+    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
+                                  scale, s2a_bwd_tile_rows());
+  return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
+                                   dq, dk, dv, delta_ws, D, p,
+                                   (hipStream_t)stream),
+                    "backward launch");
+}
+
+s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
+                            int valid_len, int *gid, int *slot, int *src,
+                            void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(1, N, 2, 16, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!gid || !slot || !src) return fail(S2A_EINVAL, "NULL map pointer");
+  if (!aligned16(gid) || !aligned16(slot) || !aligned16(src))
+    return fail(S2A_EINVAL, "map pointers must be 16-byte aligned");
+  const S2AGeom g = make_geom(N, G, shift, boundary, valid_len);
+  return hip_status(s2a_launch_map(g, gid, slot, src, (hipStream_t)stream),
+                    "group map launch");
+}
+
+const char *s2attn_strerror(int status) {
+  switch (status) {
+    case S2A_OK: return "ok";
+    case S2A_EINVAL: return "invalid argument";
+    case S2A_EUNSUPPORTED: return "unsupported head width";
+    case S2A_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char *s2attn_last_error(void) { return g_err; }
+
+const char *s2attn_version(void) { return "s2attn 0.1.0 gfx950"; }
+
+}  // extern "C"

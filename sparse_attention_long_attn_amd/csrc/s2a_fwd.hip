@@ -1,0 +1,275 @@
+// Forward of shifted sparse attention on gfx950.
+//
+// One workgroup (4 waves) computes 128 query rows of one group of one
+// (batch, head): every query's visible set is the keys of its own group at
+// or before it in group order whose position is below the valid length
+// (PaperTrace "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调", §1, visible sets
+// N_0(i), N_1(i) and the cyclic-shift paragraph).  Only the key tiles of
+// that group up to the diagonal are visited, so the work is proportional
+// to the allowed pairs, not to N^2 (§1.1, last paragraph).
+//
+// Per key tile of 64 keys:
+//   S^T = K Q^T           bf16 MFMA 32x32x16, fp32 accumulate; each lane
+//                         owns one query column, so the row max needs a
+//                         single cross-lane exchange (lane l <-> l^32)
+//   online softmax        fp32, base 2 with log2(e) folded into the scale
+//   O^T += V^T P^T        bf16 MFMA; V^T operands come straight from the
+//                         row-major V tile in LDS through ds_read_tr16_b64,
+//                         P^T from the S^T accumulators (same key order)
+// and the epilogue writes O and the natural-log LSE at the rows' original
+// positions (the inverse shift costs nothing: addresses come from
+// s2a_slot_pos()).
+#include "s2a_device.h"
+#include "s2a_kernels.h"
+
+namespace {
+
+constexpr int FWD_BQ = 128;  // query rows per workgroup, 32 per wave
+constexpr int FWD_BK = 64;   // keys per LDS tile
+constexpr int FWD_THREADS = 256;
+
+template <int D>
+struct FwdDims {
+  static constexpr int DP = D < 32 ? 32 : D;  // width in LDS (32-blocks)
+  static constexpr int KP = DP + 16;          // LDS row pitch, elements
+  static constexpr int KSTEPS = D / 16;       // 16-wide steps over d
+  static constexpr int DB = DP / 32;          // 32-wide blocks over d
+  static constexpr int CPR = DP / 8;          // 16-byte chunks per row
+};
+
+// True if the key slots [k0, kend) of a group hold a position >= L.
+__device__ __forceinline__ bool tile_has_padding(int base, int k0, int kend,
+                                                 int N, int L) {
+  if (L >= N) return false;
+  const int first = s2a_slot_pos(base, k0, N);
+  const int last = s2a_slot_pos(base, kend - 1, N);
+  return last >= first ? last >= L : true;  // a wrapped tile holds N-1
+}
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(FWD_THREADS, 1) void s2a_fwd_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, void *__restrict__ o,
+    float *__restrict__ lse, S2AParams p) {
+  using Dm = FwdDims<D>;
+  constexpr int KP = Dm::KP;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[FWD_BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[FWD_BK * KP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  // Workgroup -> (unit, query tile).  Consecutive workgroup ids go to the
+  // 8 XCDs in turn, so ids equal mod 8 share an XCD and its L2: all tiles
+  // of one (batch, head, group) unit run there, heaviest (last) tile first.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, jj = bid >> 3;
+  const int lu = jj / p.tiles;
+  const int tile = p.tiles - 1 - (jj - lu * p.tiles);
+  const int u = lu * 8 + xcd;
+  if (u >= p.units) return;
+  const int gi = u % p.ngmax;
+  const int bh = u / p.ngmax;
+  const int h = bh % p.H, b = bh / p.H;
+  const int cls = h >= (p.H >> 1);
+  int base, glen;
+  if (!s2a_group(p.g, cls, gi, base, glen)) return;
+  const int q0 = tile * FWD_BQ;
+  if (q0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;  // elements between consecutive positions
+  const size_t boff = (size_t)b * N * rs + (size_t)h * D;
+
+  // This lane's query (one column of S^T).
+  const int qslot = q0 + 32 * w + l32;
+  const bool qin = qslot < glen;
+  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const bool qvalid = qin && qpos < L;
+
+  bf16x8 qreg[Dm::KSTEPS];
+  {
+    const bf16_t *qrow = q + boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int t = 0; t < Dm::KSTEPS; ++t) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qin) raw = *(const u32x4 *)(qrow + 16 * t + 8 * hf);
+      qreg[t] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x16 oacc[Dm::DB];
+#pragma unroll
+  for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = min(glen, q0 + FWD_BQ);
+  const int wq_lo = q0 + 32 * w;
+  const int wq_hi = wq_lo + 31;
+  const float c2 = p.scale_log2;
+
+  for (int k0 = 0; k0 < kend; k0 += FWD_BK) {
+    __syncthreads();  // previous tile fully consumed
+    for (int c = tid; c < FWD_BK * Dm::CPR; c += FWD_THREADS) {
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      const int ks = k0 + r;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (ks < glen && ch * 8 < D) {
+        const int kp = s2a_slot_pos(base, ks, N);
+        if (kp < L) {  // padded keys stay zero in LDS
+          const size_t off = boff + (size_t)kp * rs + ch * 8;
+          kv = *(const u32x4 *)(k + off);
+          vv = *(const u32x4 *)(v + off);
+        }
+      }
+      *(u32x4 *)(Ks + r * KP + ch * 8) = kv;
+      *(u32x4 *)(Vs + r * KP + ch * 8) = vv;
+    }
+    __syncthreads();
+    if (k0 > wq_hi) continue;  // every query of this wave precedes the tile
+
+    // S^T = K Q^T for 64 keys x 32 queries.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+      for (int t = 0; t < Dm::KSTEPS; ++t) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8,
+            *(const u32x4 *)(Ks + (32 * kb + l32) * KP + 16 * t + 8 * hf));
+        sacc[kb] = mfma32(a, qreg[t], sacc[kb]);
+      }
+    }
+
+    // Mask where the tile crosses the diagonal, the group end or padding.
+    const int kstop = min(k0 + FWD_BK, glen);
+    const bool edge = (k0 + FWD_BK - 1 > wq_lo) || (k0 + FWD_BK > glen) ||
+                      tile_has_padding(base, k0, kstop, N, L);
+    if (edge) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const bool ok =
+              ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
+          if (!ok) sacc[kb][i] = -INFINITY;
+        }
+    }
+
+    // Online softmax (base 2).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -m_use));
+        sacc[kb][i] = e;
+        ls += e;
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+    // O^T += V^T P^T, 16 keys per MFMA.  Key order inside a step: element
+    // j of half hf is key 16*ks + 8*(j/4) + 4*hf + j%4 on both operands.
+    const int grp = lane >> 4;
+    const int trow = 4 * hf + ((lane & 15) >> 2);
+    const int tcol = 16 * (grp & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int ks = 0; ks < FWD_BK / 16; ++ks) {
+      const f32x16 &sp = sacc[ks >> 1];
+      const int e0 = 8 * (ks & 1);
+      const bf16x8 pb = to_bf16x8(sp[e0 + 0], sp[e0 + 1], sp[e0 + 2],
+                                  sp[e0 + 3], sp[e0 + 4], sp[e0 + 5],
+                                  sp[e0 + 6], sp[e0 + 7]);
+      const bf16_t *vr = Vs + (16 * ks + trow) * KP + tcol;
+#pragma unroll
+      for (int db = 0; db < Dm::DB; ++db) {
+        const bf16x4 lo = lds_read_tr(vr + 32 * db);
+        const bf16x4 hi = lds_read_tr(vr + 8 * KP + 32 * db);
+        oacc[db] = mfma32(cat4(lo, hi), pb, oacc[db]);
+      }
+    }
+  }
+
+  // Epilogue: normalise, write O and LSE at the original position.
+  const float lt = l_run + wave_xor32(l_run);
+  if (qin) {
+    const float inv = qvalid ? 1.f / lt : 0.f;
+    const size_t orow = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        if (d < D) {
+          float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+          if (qvalid) {
+            r0 = oacc[db][4 * i4 + 0] * inv;
+            r1 = oacc[db][4 * i4 + 1] * inv;
+            r2 = oacc[db][4 * i4 + 2] * inv;
+            r3 = oacc[db][4 * i4 + 3] * inv;
+          }
+          if (OF32) {
+            f32x4 val = {r0, r1, r2, r3};
+            *(f32x4 *)((float *)o + orow + d) = val;
+          } else {
+            *(bf16x4 *)((bf16_t *)o + orow + d) = to_bf16x4(r0, r1, r2, r3);
+          }
+        }
+      }
+    if (hf == 0)
+      lse[((size_t)b * p.H + h) * N + qpos] =
+          qvalid ? (m_run + __builtin_amdgcn_logf(lt)) * S2A_LN2 : -INFINITY;
+  }
+}
+
+template <int D, bool OF32>
+hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
+                        float *lse, const S2AParams &p, hipStream_t st) {
+  const int units_pad = (p.units + 7) / 8 * 8;
+  dim3 grid((unsigned)units_pad * (unsigned)p.tiles), block(FWD_THREADS);
+  const bf16_t *qq = (const bf16_t *)q, *kk = (const bf16_t *)k,
+               *vv = (const bf16_t *)v;
+  S2AParams pp = p;
+  void *args[] = {(void *)&qq, (void *)&kk, (void *)&vv, (void *)&o,
+                  (void *)&lse, (void *)&pp};
+  return hipLaunchKernel((const void *)s2a_fwd_kernel<D, OF32>, grid, block,
+                         args, 0, st);
+}
+
+}  // namespace
+
+int s2a_fwd_tile_rows() { return FWD_BQ; }
+
+hipError_t s2a_launch_fwd(const void *q, const void *k, const void *v,
+                          void *o, bool o_f32, float *lse, int D,
+                          const S2AParams &p, hipStream_t st) {
+  switch (D) {
+    case 16: return o_f32 ? launch_fwd_t<16, true>(q, k, v, o, lse, p, st)
+                          : launch_fwd_t<16, false>(q, k, v, o, lse, p, st);
+    case 32: return o_f32 ? launch_fwd_t<32, true>(q, k, v, o, lse, p, st)
+                          : launch_fwd_t<32, false>(q, k, v, o, lse, p, st);
+    case 64: return o_f32 ? launch_fwd_t<64, true>(q, k, v, o, lse, p, st)
+                          : launch_fwd_t<64, false>(q, k, v, o, lse, p, st);
+    case 128: return o_f32 ? launch_fwd_t<128, true>(q, k, v, o, lse, p, st)
+                           : launch_fwd_t<128, false>(q, k, v, o, lse, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}

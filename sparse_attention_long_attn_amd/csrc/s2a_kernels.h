@@ -1,0 +1,23 @@
+// Launch entry points of the kernels (host side of the library).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "s2a_geom.h"
+
+struct S2AParams;
+
+int s2a_fwd_tile_rows();  // query rows per forward workgroup
+int s2a_bwd_tile_rows();  // key rows per backward workgroup
+
+hipError_t s2a_launch_fwd(const void *q, const void *k, const void *v,
+                          void *o, bool o_f32, float *lse, int D,
+                          const S2AParams &p, hipStream_t st);
+
+hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
+                          const void *o, bool o_f32, const float *lse,
+                          const void *dout, float *dq, float *dk, float *dv,
+                          float *delta, int D, const S2AParams &p,
+                          hipStream_t st);
+
+hipError_t s2a_launch_map(const S2AGeom &g, int *gid, int *slot, int *src,
+                          hipStream_t st);

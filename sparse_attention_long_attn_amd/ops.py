@@ -1,0 +1,151 @@
+"""Thin torch-facing wrappers of the C ABI: argument marshalling only.
+
+Every step of the computation runs in the HIP library; torch provides the
+device memory and the current stream.  Nothing here computes attention,
+and there is no CPU fallback: without the built library these functions
+raise.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+BOUNDARIES = {"wrap": _lib.S2A_WRAP, "split": _lib.S2A_SPLIT,
+              _lib.S2A_WRAP: _lib.S2A_WRAP, _lib.S2A_SPLIT: _lib.S2A_SPLIT}
+
+
+def _boundary(b) -> int:
+    try:
+        return BOUNDARIES[b]
+    except KeyError:
+        raise ValueError(f"boundary must be 'wrap' or 'split', got {b!r}")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _check_qkv(*ts, shape=None):
+    shape = shape or ts[0].shape
+    if len(shape) != 4:
+        raise ValueError("q, k, v must be [B, N, H, D]")
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v, dout must be bfloat16")
+        if t.shape != shape:
+            raise ValueError(f"shape mismatch: {tuple(t.shape)} vs {tuple(shape)}")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return shape
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
+        valid_len: int | None = None, scale: float | None = None,
+        out_dtype=torch.float32, o=None, lse=None):
+    """S²-Attn forward.  Returns (o [B,N,H,D], lse [B,H,N] float32)."""
+    B, N, H, D = _check_qkv(q, k, v)
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if o is None:
+        o = torch.empty((B, N, H, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if o.dtype != out_dtype or o.shape != q.shape or not o.is_contiguous():
+        raise ValueError("o must be a contiguous [B,N,H,D] tensor of out_dtype")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
+    odt = _lib.S2A_F32 if out_dtype == torch.float32 else _lib.S2A_BF16
+    lib = _lib.load()
+    _lib.check(lib.s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
+                              _ptr(lse), B, N, H, D, G, shift,
+                              _boundary(boundary), valid_len, scale,
+                              _stream(q.device)))
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
+        boundary="wrap", valid_len: int | None = None,
+        scale: float | None = None, dq=None, dk=None, dv=None, delta=None):
+    """S²-Attn backward from the forward's o and lse.
+    Returns (dq, dk, dv), float32 [B,N,H,D]."""
+    B, N, H, D = _check_qkv(q, k, v, dout)
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
+            or not o.is_contiguous():
+        raise ValueError("o must be a contiguous [B,N,H,D] float32/bfloat16 tensor")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
+    mk = lambda: torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous float32 [B,N,H,D]")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
+    lib = _lib.load()
+    _lib.check(lib.s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
+                              _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(delta), B, N, H, D, G, shift,
+                              _boundary(boundary), valid_len, scale,
+                              _stream(q.device)))
+    return dq, dk, dv
+
+
+def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
+              valid_len: int | None = None, device="cuda"):
+    """Group index maps (gid, slot, src), each int32 [2, N] on the device."""
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    outs = [torch.empty((2, N), dtype=torch.int32, device=device)
+            for _ in range(3)]
+    lib = _lib.load()
+    _lib.check(lib.s2attn_group_map(N, G, shift, _boundary(boundary),
+                                    valid_len, *(_ptr(t) for t in outs),
+                                    _stream(outs[0].device)))
+    return tuple(outs)
+
+
+class S2AttnFunction(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in the library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, G, shift, boundary, valid_len, scale):
+        o, lse = fwd(q, k, v, G=G, shift=shift, boundary=boundary,
+                     valid_len=valid_len, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (G, shift, boundary, valid_len, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        G, shift, boundary, valid_len, scale = ctx.cfg
+        dq, dk, dv = bwd(q, k, v, o, lse,
+                         do.to(torch.bfloat16).contiguous(), G=G,
+                         shift=shift, boundary=boundary, valid_len=valid_len,
+                         scale=scale)
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype),
+                None, None, None, None, None)
+
+
+def s2_attention(q, k, v, G, shift=None, boundary="wrap", valid_len=None,
+                 scale=None):
+    """Differentiable S²-Attn (float32 output)."""
+    return S2AttnFunction.apply(q, k, v, G, shift, boundary, valid_len, scale)

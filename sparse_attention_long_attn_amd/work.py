@@ -1,0 +1,77 @@
+"""Host-side work accounting: allowed pairs, useful FLOPs, algorithmic bytes.
+
+Pair counts are the closed forms of the edge sets (PaperTrace "4.1.2 ·
+LongLoRA: 用S²-Attn完成长上下文微调", §1, complexity paragraph: a group of
+length n holds n(n+1)/2 causal pairs, so a class of M full groups holds
+M*G*(G+1)/2 ~ NG/2).  With a valid length L < N, a group's pairs are those
+among its valid members in group order.  Useful FLOPs count 4*D per allowed
+pair for the forward (2D for QK^T, 2D for PV) and 10*D for the backward.
+"""
+from __future__ import annotations
+
+WRAP, SPLIT = 0, 1
+
+
+def _groups(N, G, shift, boundary, cls):
+    """(start position, length, wrapped) of each group of a head class."""
+    M = N // G
+    s = 0 if M == 1 else shift
+    if cls == 0 or s == 0:
+        return [(g * G, G) for g in range(M)]
+    if boundary == WRAP:
+        return [(g * G + s, G) for g in range(M)]
+    return [(0, s)] + [(s + g * G, G) for g in range(M - 1)] + [(N - s, s)]
+
+
+def _pairs_in_group(base, n, N, L):
+    """Causal pairs among the valid members of a group whose slot j holds
+    position (base + j) mod N."""
+    # valid slots form at most two runs; pairs = sum over valid slots j of
+    # (number of valid slots <= j)
+    tot = 0
+    cnt = 0
+    # walk runs rather than slots: slots [0, n) map to [base, base+n) mod N
+    runs = []
+    if base + n <= N:
+        runs.append((base, base + n))
+    else:
+        runs.append((base, N))
+        runs.append((0, base + n - N))
+    for a, b in runs:
+        v = max(0, min(b, L) - a)      # valid positions of the run
+        tot += v * cnt + v * (v + 1) // 2
+        cnt += v
+    return tot
+
+
+def allowed_pairs(N, G, shift, boundary, L):
+    """Allowed (query, key) pairs per head of class 0 and class 1."""
+    out = []
+    for cls in (0, 1):
+        out.append(sum(_pairs_in_group(b, n, N, L)
+                       for b, n in _groups(N, G, shift, boundary, cls)))
+    return tuple(out)
+
+
+def total_pairs(B, N, H, G, shift, boundary, L):
+    c0, c1 = allowed_pairs(N, G, shift, boundary, L)
+    return B * (H // 2) * (c0 + c1)
+
+
+def useful_flops(B, N, H, D, G, shift, boundary, L):
+    """(forward, backward) useful FLOPs: 4*D and 10*D per allowed pair."""
+    p = total_pairs(B, N, H, G, shift, boundary, L)
+    return 4 * D * p, 10 * D * p
+
+
+def algorithmic_bytes(B, N, H, D, o_bytes=4):
+    """(forward, backward) minimum HBM bytes of one pass.
+
+    forward : read q, k, v (bf16); write o and lse
+    backward: read q, k, v, dout (bf16), o, lse; write delta then read it;
+              write dq, dk, dv (fp32)"""
+    e = B * N * H * D
+    rows = B * H * N
+    fwd = 3 * 2 * e + o_bytes * e + 4 * rows
+    bwd = 4 * 2 * e + o_bytes * e + 3 * 4 * e + 3 * 4 * rows
+    return fwd, bwd

@@ -1,0 +1,124 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every
+function include/s2attn.h declares, and rejects bad arguments with the
+documented status before touching the device.  Also pins the host-side
+work accounting against the oracle's enumerated pair counts."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from sparse_attention_long_attn_amd import _lib, work
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "s2attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    fns = header_functions()
+    for name in ("s2attn_fwd", "s2attn_bwd", "s2attn_group_map"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) <= set(_lib.EXPORTS)
+
+
+NULL = None
+OK_ARGS = dict(B=1, N=64, H=4, D=16, G=16, shift=8, boundary=0, L=64,
+               scale=0.25)
+
+
+def call_fwd(**kw):
+    a = dict(OK_ARGS, **kw)
+    lib = _lib.load()
+    return lib.s2attn_fwd(NULL, NULL, NULL, NULL, 1, NULL, a["B"], a["N"],
+                          a["H"], a["D"], a["G"], a["shift"], a["boundary"],
+                          a["L"], a["scale"], NULL)
+
+
+def call_bwd(**kw):
+    a = dict(OK_ARGS, **kw)
+    lib = _lib.load()
+    return lib.s2attn_bwd(NULL, NULL, NULL, NULL, 1, NULL, NULL, NULL, NULL,
+                          NULL, NULL, a["B"], a["N"], a["H"], a["D"], a["G"],
+                          a["shift"], a["boundary"], a["L"], a["scale"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=3), _lib.S2A_EINVAL),
+    (dict(G=15, shift=7), _lib.S2A_EINVAL),
+    (dict(N=60), _lib.S2A_EINVAL),
+    (dict(L=0), _lib.S2A_EINVAL),
+    (dict(L=65), _lib.S2A_EINVAL),
+    (dict(shift=4), _lib.S2A_EINVAL),
+    (dict(boundary=2), _lib.S2A_EINVAL),
+    (dict(B=0), _lib.S2A_EINVAL),
+    (dict(D=24), _lib.S2A_EUNSUPPORTED),
+    (dict(D=256), _lib.S2A_EUNSUPPORTED),
+    (dict(), _lib.S2A_EINVAL),          # valid shape, NULL pointers
+])
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_bad_arguments_rejected_before_launch(kw, status, call):
+    assert call(**kw) == status
+    assert _lib.load().s2attn_last_error().decode() != ""
+
+
+def test_misaligned_pointer_rejected():
+    lib = _lib.load()
+    buf = (ctypes.c_char * 4096)()
+    base = ctypes.addressof(buf)
+    p = ((base + 15) // 16) * 16
+    st = lib.s2attn_fwd(p + 2, p, p, p, 1, p, 1, 64, 4, 16, 16, 8, 0, 64,
+                        0.25, None)
+    assert st == _lib.S2A_EINVAL
+    assert "aligned" in lib.s2attn_last_error().decode()
+    st = lib.s2attn_fwd(p, p, p, p, 1, p, 1, 64, 4, 16, 16, 8, 0, 64,
+                        float("nan"), None)
+    assert st == _lib.S2A_EINVAL
+
+
+def test_group_map_rejects_bad_shapes():
+    lib = _lib.load()
+    assert lib.s2attn_group_map(60, 16, 8, 0, 60, None, None, None, None) \
+        == _lib.S2A_EINVAL
+    assert lib.s2attn_group_map(64, 16, 8, 0, 64, None, None, None, None) \
+        == _lib.S2A_EINVAL
+
+
+def test_strerror():
+    lib = _lib.load()
+    for st in range(4):
+        assert lib.s2attn_strerror(st)
+    with pytest.raises(ValueError):
+        _lib.check(_lib.S2A_EINVAL)
+    with pytest.raises(_lib.S2AttnError):
+        _lib.check(_lib.S2A_EHIP)
+
+
+@pytest.mark.parametrize("N,G,L", [(64, 16, 64), (64, 16, 50), (64, 16, 5),
+                                   (48, 12, 37), (96, 32, 81), (128, 128, 100),
+                                   (256, 64, 200), (256, 64, 250)])
+@pytest.mark.parametrize("boundary", [0, 1])
+@pytest.mark.parametrize("half", [0, 1])
+def test_work_pairs_match_oracle_enumeration(N, G, L, boundary, half):
+    shift = half * G // 2
+    assert work.allowed_pairs(N, G, shift, boundary, L) == \
+        oracle.allowed_pairs(N, G, shift, boundary, L)
+
+
+def test_work_pairs_of_the_headline_workload():
+    # N=32768, G=8192, WRAP: both classes M*G*(G+1)/2
+    c0, c1 = work.allowed_pairs(32768, 8192, 4096, 0, 32768)
+    assert c0 == c1 == 4 * 8192 * 8193 // 2
+    fwd, bwd = work.useful_flops(1, 32768, 32, 128, 8192, 4096, 0, 32768)
+    assert fwd == 4 * 128 * 16 * (c0 + c1) and bwd == 2.5 * fwd
