@@ -1,0 +1,225 @@
+#!/usr/bin/env python
+"""Throughput of shifted sparse attention (S²-Attn) forward + backward on one
+MI355X, in useful TFLOP/s.
+
+Workload: one Llama-2-7B-shaped attention layer, B=1, N=32768, H=32,
+D=128, group G=8192 (ratio 1/4, shift 4096), original wrapped-roll
+boundary; seeded synthetic bf16 N(0,1) q, k, v, dO resident in HBM before
+the timed region.  A step is one forward (O fp32, LSE) plus one backward
+(delta preprocess, then dQ/dK/dV).  Useful FLOPs count 4*D per allowed
+causal pair for the forward and 10*D for the backward.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
+on the stream the library launches on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+WORKLOAD = dict(config=3, B=1, N=32768, H=32, D=128, G=8192, boundary=0,
+                L=32768)
+# CPU-baseline sample: every query row of one head of each class (fwd+bwd),
+# i.e. 2 of the 32 heads
+CPU_SAMPLE_ROWS = 32768
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "sparse_attention_long_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 PMC
+    summary, or None if there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg):
+    """Time the float64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover - informational only
+        threads = len(os.sched_getaffinity(0))
+    B, N, H, D, G = cfg["B"], cfg["N"], cfg["H"], cfg["D"], cfg["G"]
+    heads = [0, H // 2]                       # one head of each class
+    R = CPU_SAMPLE_ROWS
+    ins = syn.make_inputs(cfg["config"], 0, B, N, H, D, with_do=True,
+                          L=cfg["L"])
+    x = [syn.bf16_bits_to_f64(ins[t][:, :, heads, :])
+         for t in ("q", "k", "v", "do")]
+    rows = np.arange(R)
+    t0 = time.perf_counter()
+    oracle.backward(*x, G, G // 2, cfg["boundary"], cfg["L"],
+                    1.0 / D ** 0.5, rows=rows)
+    dt = time.perf_counter() - t0
+    # allowed pairs of rows [0, R) in each of the two heads
+    pairs = sum(int(oracle.adjacency_block(c, rows, N, G, G // 2,
+                                           cfg["boundary"], cfg["L"]).sum())
+                for c in (0, 1))
+    flops = 14 * D * pairs * B
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"float64 oracle fwd+bwd of query rows [0,{R}) of heads "
+                      f"{heads} (one per head class), B={B} N={N} D={D} "
+                      f"G={G} wrap: {pairs} allowed pairs"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this engine has no multi-GPU "
+              "path (heads shard with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    from sparse_attention_long_attn_amd import work
+
+    cfg = WORKLOAD
+    B, N, H, D, G, L, bnd = (cfg[k] for k in ("B", "N", "H", "D", "G", "L",
+                                              "boundary"))
+    shift = G // 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ins = syn.make_inputs(cfg["config"], 0, B, N, H, D, with_do=True, L=L)
+    q, k, v, do = (torch.from_numpy(ins[t].view("int16")).view(torch.bfloat16)
+                   .to(dev) for t in ("q", "k", "v", "do"))
+    del ins
+    o = torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+                  for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    kw = dict(G=G, shift=shift, boundary=bnd, valid_len=L)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        s2a.fwd(q, k, v, o=o, lse=lse, **kw)
+        if ev is not None:
+            ev[1].record()
+        s2a.bwd_preprocess(o, do, dq, delta)
+        if ev is not None:
+            ev[2].record()
+        s2a.bwd_main(q, k, v, lse, delta, do, dq, dk, dv, **kw)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    pre_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    main_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+
+    f_fwd, f_bwd = work.useful_flops(B, N, H, D, G, shift, bnd, L)
+    b_fwd, b_bwd = work.algorithmic_bytes(B, N, H, D, o_bytes=4)
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    kernels = {
+        "s2a_fwd_kernel": (fwd_ms, f_fwd),
+        "s2a_bwd_kernel": (main_ms, f_bwd),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dms, dfl = kernels[dom]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(dom),
+                "avg_ms": round(dms, 4),
+                "flops_per_launch": dfl}
+
+    out = {
+        "metric": "S²-Attn fwd+bwd useful TFLOP/s and % bf16 MFMA peak at "
+                  "N=32K, G=8K",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 q,k,v,dO (PCG64, rounded to "
+                "nearest even)",
+        "config": {"workload": "S2-Attn fwd+bwd, Llama-2-7B layer shape, "
+                               "B=1 N=32768 H=32 D=128 G=8192 shift=4096 "
+                               "wrapped-roll boundary",
+                   "global_batch": B, "seq_len": N, "heads": H,
+                   "head_dim": D, "group": G, "boundary": "wrap",
+                   "valid_len": L, "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_preprocess_ms": round(pre_ms, 4),
+        "bwd_main_ms": round(main_ms, 4),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((pre_ms + main_ms) * 1e-3) / 1e12, 2),
+        "useful_flops_per_step": f_fwd + f_bwd,
+        "algorithmic_bytes": {"fwd": b_fwd, "bwd": b_bwd},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,6 +102,25 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       void *stream);
 
 /*
+ * The two stages of s2attn_bwd, for callers that schedule or time them
+ * separately.  s2attn_bwd_preprocess writes delta_ws[b,h,x] = dout[x].o[x]
+ * and clears dq; s2attn_bwd_main then accumulates dq and writes dk, dv.
+ * Calling both in this order on one stream equals s2attn_bwd.  Arguments,
+ * layouts and checks are those of s2attn_bwd.
+ */
+s2a_status s2attn_bwd_preprocess(const void *o, int o_dtype,
+                                 const void *dout, float *dq,
+                                 float *delta_ws, int B, int N, int H, int D,
+                                 void *stream);
+
+s2a_status s2attn_bwd_main(const void *q, const void *k, const void *v,
+                           const float *lse, const float *delta_ws,
+                           const void *dout, float *dq, float *dk, float *dv,
+                           int B, int N, int H, int D, int G, int shift,
+                           int boundary, int valid_len, float scale,
+                           void *stream);
+
+/*
  * Group index maps, computed on the device by the same group geometry the
  * attention kernels use.  For head class c (0: heads < H/2, 1: the rest)
  * and original position x:

@@ -16,7 +16,8 @@ S2A_OK, S2A_EINVAL, S2A_EUNSUPPORTED, S2A_EHIP = 0, 1, 2, 3
 S2A_WRAP, S2A_SPLIT = 0, 1
 S2A_BF16, S2A_F32 = 0, 1
 
-EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_group_map", "s2attn_strerror",
+EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
+           "s2attn_bwd_main", "s2attn_group_map", "s2attn_strerror",
            "s2attn_last_error", "s2attn_version")
 
 _lib = None
@@ -42,6 +43,11 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
                                I, I, I, I, I, I, I, I, F, P]
     lib.s2attn_bwd.restype = I
+    lib.s2attn_bwd_preprocess.argtypes = [P, I, P, P, P, I, I, I, I, P]
+    lib.s2attn_bwd_preprocess.restype = I
+    lib.s2attn_bwd_main.argtypes = [P, P, P, P, P, P, P, P, P,
+                                    I, I, I, I, I, I, I, I, F, P]
+    lib.s2attn_bwd_main.restype = I
     lib.s2attn_group_map.argtypes = [I, I, I, I, I, P, P, P, P]
     lib.s2attn_group_map.restype = I
     lib.s2attn_strerror.argtypes = [I]

@@ -364,21 +364,14 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v,
 
 int s2a_bwd_tile_rows() { return BWD_BK; }
 
-hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
-                          const void *o, bool o_f32, const float *lse,
-                          const void *dout, float *dq, float *dk, float *dv,
-                          float *delta, int D, const S2AParams &p,
-                          hipStream_t st) {
-  hipError_t e;
+hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
+                              float *dq, float *delta, int B, int N, int H,
+                              int D, hipStream_t st) {
   switch (D) {
-#define S2A_CASE(DD)                                                        \
-  case DD:                                                                  \
-    e = o_f32 ? launch_pre_t<DD, true>(o, dout, delta, dq, p.B, p.g.N, p.H, \
-                                       st)                                  \
-              : launch_pre_t<DD, false>(o, dout, delta, dq, p.B, p.g.N,     \
-                                        p.H, st);                           \
-    if (e != hipSuccess) return e;                                          \
-    return launch_bwd_t<DD>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+#define S2A_CASE(DD)                                                       \
+  case DD:                                                                 \
+    return o_f32 ? launch_pre_t<DD, true>(o, dout, delta, dq, B, N, H, st)  \
+                 : launch_pre_t<DD, false>(o, dout, delta, dq, B, N, H, st);
     S2A_CASE(16)
     S2A_CASE(32)
     S2A_CASE(64)
@@ -386,4 +379,29 @@ hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
 #undef S2A_CASE
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t s2a_launch_bwd_main(const void *q, const void *k, const void *v,
+                               const float *lse, const float *delta,
+                               const void *dout, float *dq, float *dk,
+                               float *dv, int D, const S2AParams &p,
+                               hipStream_t st) {
+  switch (D) {
+    case 16: return launch_bwd_t<16>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+    case 32: return launch_bwd_t<32>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+    case 64: return launch_bwd_t<64>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+    case 128: return launch_bwd_t<128>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
+                          const void *o, bool o_f32, const float *lse,
+                          const void *dout, float *dq, float *dk, float *dv,
+                          float *delta, int D, const S2AParams &p,
+                          hipStream_t st) {
+  const hipError_t e =
+      s2a_launch_bwd_pre(o, o_f32, dout, dq, delta, p.B, p.g.N, p.H, D, st);
+  if (e != hipSuccess) return e;
+  return s2a_launch_bwd_main(q, k, v, lse, delta, dout, dq, dk, dv, D, p, st);
 }

@@ -19,5 +19,15 @@ hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
                           float *delta, int D, const S2AParams &p,
                           hipStream_t st);
 
+hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
+                              float *dq, float *delta, int B, int N, int H,
+                              int D, hipStream_t st);
+
+hipError_t s2a_launch_bwd_main(const void *q, const void *k, const void *v,
+                               const float *lse, const float *delta,
+                               const void *dout, float *dq, float *dk,
+                               float *dv, int D, const S2AParams &p,
+                               hipStream_t st);
+
 hipError_t s2a_launch_map(const S2AGeom &g, int *gid, int *slot, int *src,
                           hipStream_t st);
