@@ -93,12 +93,15 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
     S2AParams p) {
   using Dm = BwdDims<D>;
   constexpr int KP = Dm::KP, SP = Dm::SP;
+  constexpr int QT = BWD_BQ * KP;                        // elements per buffer
+  constexpr int NCH = BWD_BQ * Dm::CPR / BWD_THREADS;    // chunks per thread
+  static_assert(BWD_BQ * Dm::CPR % BWD_THREADS == 0, "tile split");
   __shared__ __attribute__((aligned(16))) bf16_t Ksm[BWD_BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[BWD_BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t dOs[BWD_BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[2 * QT];
+  __shared__ __attribute__((aligned(16))) bf16_t dOs[2 * QT];
   __shared__ __attribute__((aligned(16))) bf16_t dSt[BWD_BK * SP];
-  __shared__ __attribute__((aligned(16))) float lse2s[BWD_BQ];
-  __shared__ __attribute__((aligned(16))) float dlts[BWD_BQ];
+  __shared__ __attribute__((aligned(16))) float lse2s[2 * BWD_BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[2 * BWD_BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -162,18 +165,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
     *(u32x4 *)(Ksm + r * KP + ch * 8) = kv;
   }
 
-  f32x16 dkacc[Dm::DB], dvacc[Dm::DB];
+  // Query-tile staging through registers.  Rows outside the group or padded
+  // get q = dO = 0, lse = +inf (so P = 0) and delta = 0 (so dS = 0).
+  u32x4 qst[NCH], gst[NCH];
+  float l2st = INFINITY, dlst = 0.f;
+  auto fetch = [&](int q0) {
 #pragma unroll
-  for (int db = 0; db < Dm::DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dkacc[db][i] = 0.f;
-      dvacc[db][i] = 0.f;
-    }
-
-  for (int q0 = k0; q0 < glen; q0 += BWD_BQ) {
-    __syncthreads();  // previous Q/dO/dS^T tiles fully consumed
-    for (int c = tid; c < BWD_BQ * Dm::CPR; c += BWD_THREADS) {
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * BWD_THREADS;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       const int qsl = q0 + r;
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
@@ -185,23 +184,59 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
           gv = *(const u32x4 *)(dout + off);
         }
       }
-      *(u32x4 *)(Qs + r * KP + ch * 8) = qv;
-      *(u32x4 *)(dOs + r * KP + ch * 8) = gv;
+      qst[i] = qv;
+      gst[i] = gv;
     }
     if (tid < BWD_BQ) {
       const int qsl = q0 + tid;
-      float l2 = INFINITY, dl = 0.f;  // rows outside the group or padded:
-      if (qsl < glen) {               // P = exp2(x - inf) = 0, dS = 0
+      l2st = INFINITY;
+      dlst = 0.f;
+      if (qsl < glen) {
         const int qp = s2a_slot_pos(base, qsl, N);
         if (qp < L) {
-          l2 = lse[lrow + qp] * S2A_LOG2E;
-          dl = delta[lrow + qp];
+          l2st = lse[lrow + qp] * S2A_LOG2E;
+          dlst = delta[lrow + qp];
         }
       }
-      lse2s[tid] = l2;
-      dlts[tid] = dl;
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * BWD_THREADS;
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      *(u32x4 *)(Qs + buf * QT + r * KP + ch * 8) = qst[i];
+      *(u32x4 *)(dOs + buf * QT + r * KP + ch * 8) = gst[i];
+    }
+    if (tid < BWD_BQ) {
+      lse2s[buf * BWD_BQ + tid] = l2st;
+      dlts[buf * BWD_BQ + tid] = dlst;
+    }
+  };
+
+  f32x16 dkacc[Dm::DB], dvacc[Dm::DB];
+#pragma unroll
+  for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  const int nq = (glen - k0 + BWD_BQ - 1) / BWD_BQ;  // query tiles from k0
+  fetch(k0);
+  stage(0);
+  __syncthreads();
+
+  for (int it = 0; it < nq; ++it) {
+    const int q0 = k0 + it * BWD_BQ;
+    const int buf = it & 1;
+    const bool more = it + 1 < nq;
+    if (more) fetch(q0 + BWD_BQ);  // in flight during this tile's math
+    const bf16_t *Qb = Qs + buf * QT;
+    const bf16_t *dOb = dOs + buf * QT;
+    const float *l2b = lse2s + buf * BWD_BQ;
+    const float *dlb = dlts + buf * BWD_BQ;
 
     const bool active = q0 + BWD_BQ - 1 >= kw0;
     if (active) {
@@ -216,8 +251,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
 #pragma unroll
         for (int t = 0; t < Dm::KSTEPS; ++t) {
           const int ro = (32 * qb + l32) * KP + 16 * t + 8 * hf;
-          const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Qs + ro));
-          const bf16x8 ag = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dOs + ro));
+          const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Qb + ro));
+          const bf16x8 ag = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dOb + ro));
           sacc[qb] = mfma32(aq, kreg[t], sacc[qb]);
           dpacc[qb] = mfma32(ag, vreg[t], dpacc[qb]);
         }
@@ -229,8 +264,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = 32 * qb + 8 * i4 + 4 * hf;
-          const f32x4 l2 = *(const f32x4 *)(lse2s + r0);
-          const f32x4 dl = *(const f32x4 *)(dlts + r0);
+          const f32x4 l2 = *(const f32x4 *)(l2b + r0);
+          const f32x4 dl = *(const f32x4 *)(dlb + r0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
@@ -253,11 +288,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
         const int ro = (16 * qs + trow) * KP + tcol;
 #pragma unroll
         for (int db = 0; db < Dm::DB; ++db) {
-          const bf16x8 ag = cat4(lds_read_tr(dOs + ro + 32 * db),
-                                 lds_read_tr(dOs + ro + 8 * KP + 32 * db));
+          const bf16x8 ag = cat4(lds_read_tr(dOb + ro + 32 * db),
+                                 lds_read_tr(dOb + ro + 8 * KP + 32 * db));
           dvacc[db] = mfma32(ag, pb, dvacc[db]);
-          const bf16x8 aq = cat4(lds_read_tr(Qs + ro + 32 * db),
-                                 lds_read_tr(Qs + ro + 8 * KP + 32 * db));
+          const bf16x8 aq = cat4(lds_read_tr(Qb + ro + 32 * db),
+                                 lds_read_tr(Qb + ro + 8 * KP + 32 * db));
           dkacc[db] = mfma32(aq, sb, dkacc[db]);
         }
       }
@@ -278,7 +313,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
         for (int i4 = 0; i4 < 4; ++i4)
           *(bf16x4 *)(dSt + (32 * w + l32) * SP + 32 * qb + 8 * i4 + 4 * hf) = z;
     }
-    __syncthreads();
+    __syncthreads();  // dS^T complete
 
     // dQ[q][d] += dS[q][key] K[key][d] over the workgroup's 128 keys.
     for (int blk = w; blk < 2 * Dm::DB; blk += 4) {
@@ -308,6 +343,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
         }
       }
     }
+    if (more) stage(buf ^ 1);
+    __syncthreads();  // next tile staged; dS^T reads done
   }
 
   // dK, dV rows of this lane's key (padded keys get their exact zeros).

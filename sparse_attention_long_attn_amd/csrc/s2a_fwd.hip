@@ -47,14 +47,18 @@ __device__ __forceinline__ bool tile_has_padding(int base, int k0, int kend,
 }
 
 template <int D, bool OF32>
-__global__ __launch_bounds__(FWD_THREADS, 1) void s2a_fwd_kernel(
+__global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
     float *__restrict__ lse, S2AParams p) {
   using Dm = FwdDims<D>;
   constexpr int KP = Dm::KP;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[FWD_BK * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[FWD_BK * KP];
+  constexpr int TILE = FWD_BK * KP;                       // elements per buffer
+  constexpr int NCH = FWD_BK * Dm::CPR / FWD_THREADS;     // chunks per thread
+  static_assert(FWD_BK * Dm::CPR % FWD_THREADS == 0, "tile split");
+  // Two K and two V buffers: tile t+1 is written while tile t is read.
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -97,115 +101,154 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void s2a_fwd_kernel(
     }
   }
 
-  f32x16 oacc[Dm::DB];
+  // Staging of one K/V tile through registers: chunk c of the tile is row
+  // c / CPR, 16-byte column c % CPR.  Rows outside the group or at padded
+  // positions are zero.
+  u32x4 kst[NCH], vst[NCH];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int db = 0; db < Dm::DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int kend = min(glen, q0 + FWD_BQ);
-  const int wq_lo = q0 + 32 * w;
-  const int wq_hi = wq_lo + 31;
-  const float c2 = p.scale_log2;
-
-  for (int k0 = 0; k0 < kend; k0 += FWD_BK) {
-    __syncthreads();  // previous tile fully consumed
-    for (int c = tid; c < FWD_BK * Dm::CPR; c += FWD_THREADS) {
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * FWD_THREADS;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       const int ks = k0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (ks < glen && ch * 8 < D) {
         const int kp = s2a_slot_pos(base, ks, N);
-        if (kp < L) {  // padded keys stay zero in LDS
+        if (kp < L) {
           const size_t off = boff + (size_t)kp * rs + ch * 8;
           kv = *(const u32x4 *)(k + off);
           vv = *(const u32x4 *)(v + off);
         }
       }
-      *(u32x4 *)(Ks + r * KP + ch * 8) = kv;
-      *(u32x4 *)(Vs + r * KP + ch * 8) = vv;
+      kst[i] = kv;
+      vst[i] = vv;
     }
-    __syncthreads();
-    if (k0 > wq_hi) continue;  // every query of this wave precedes the tile
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * FWD_THREADS;
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      *(u32x4 *)(Ks + buf * TILE + r * KP + ch * 8) = kst[i];
+      *(u32x4 *)(Vs + buf * TILE + r * KP + ch * 8) = vst[i];
+    }
+  };
 
-    // S^T = K Q^T for 64 keys x 32 queries.
-    f32x16 sacc[2];
+  f32x16 oacc[Dm::DB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int db = 0; db < Dm::DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  // Running reference max (base 2) and this lane's partial row sum.  The
+  // reference only moves when a tile's max exceeds it by more than
+  // 2^RESCALE, so P <= 2^RESCALE and the O rescale is rarely needed.
+  constexpr float RESCALE = 8.f;
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  const int kend = min(glen, q0 + FWD_BQ);
+  const int ntiles = (kend + FWD_BK - 1) / FWD_BK;
+  const int wq_lo = q0 + 32 * w;
+  const int wq_hi = wq_lo + 31;
+  const float c2 = p.scale_log2;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+  const int tcol = 16 * (grp & 1) + 4 * (lane & 3);
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * FWD_BK;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) fetch(k0 + FWD_BK);  // in flight during this tile's math
+
+    if (k0 <= wq_hi) {  // else every query of this wave precedes the tile
+      const bf16_t *Kb = Ks + buf * TILE;
+      const bf16_t *Vb = Vs + buf * TILE;
+      // S^T = K Q^T for 64 keys x 32 queries.
+      f32x16 sacc[2];
 #pragma unroll
-      for (int t = 0; t < Dm::KSTEPS; ++t) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8,
-            *(const u32x4 *)(Ks + (32 * kb + l32) * KP + 16 * t + 8 * hf));
-        sacc[kb] = mfma32(a, qreg[t], sacc[kb]);
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < Dm::KSTEPS; ++t) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8,
+              *(const u32x4 *)(Kb + (32 * kb + l32) * KP + 16 * t + 8 * hf));
+          sacc[kb] = mfma32(a, qreg[t], sacc[kb]);
+        }
       }
-    }
 
-    // Mask where the tile crosses the diagonal, the group end or padding.
-    const int kstop = min(k0 + FWD_BK, glen);
-    const bool edge = (k0 + FWD_BK - 1 > wq_lo) || (k0 + FWD_BK > glen) ||
-                      tile_has_padding(base, k0, kstop, N, L);
-    if (edge) {
+      // Mask where the tile crosses the diagonal, the group end or padding.
+      const int kstop = min(k0 + FWD_BK, glen);
+      const bool edge = (k0 + FWD_BK - 1 > wq_lo) || (k0 + FWD_BK > glen) ||
+                        tile_has_padding(base, k0, kstop, N, L);
+      if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const bool ok =
+                ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
+            if (!ok) sacc[kb][i] = -INFINITY;
+          }
+      }
+
+      // Online softmax (base 2) with a lazily moved reference max.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = fmaxf(mx, wave_xor32(mx)) * c2;
+      if (__any(mx > m_ref + RESCALE)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha =
+            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool ok =
-              ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
-          if (!ok) sacc[kb][i] = -INFINITY;
+          const float e =
+              __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -m_use));
+          sacc[kb][i] = e;
+          ls += e;
         }
-    }
+      l_run += ls;
 
-    // Online softmax (base 2).
-    float mx = -INFINITY;
+      // O^T += V^T P^T, 16 keys per MFMA.  Key order inside a step: element
+      // j of half hf is key 16*ks + 8*(j/4) + 4*hf + j%4 on both operands.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < FWD_BK / 16; ++ks) {
+        const f32x16 &sp = sacc[ks >> 1];
+        const int e0 = 8 * (ks & 1);
+        const bf16x8 pb = to_bf16x8(sp[e0 + 0], sp[e0 + 1], sp[e0 + 2],
+                                    sp[e0 + 3], sp[e0 + 4], sp[e0 + 5],
+                                    sp[e0 + 6], sp[e0 + 7]);
+        const bf16_t *vr = Vb + (16 * ks + trow) * KP + tcol;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -m_use));
-        sacc[kb][i] = e;
-        ls += e;
-      }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < Dm::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
-    // O^T += V^T P^T, 16 keys per MFMA.  Key order inside a step: element
-    // j of half hf is key 16*ks + 8*(j/4) + 4*hf + j%4 on both operands.
-    const int grp = lane >> 4;
-    const int trow = 4 * hf + ((lane & 15) >> 2);
-    const int tcol = 16 * (grp & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int ks = 0; ks < FWD_BK / 16; ++ks) {
-      const f32x16 &sp = sacc[ks >> 1];
-      const int e0 = 8 * (ks & 1);
-      const bf16x8 pb = to_bf16x8(sp[e0 + 0], sp[e0 + 1], sp[e0 + 2],
-                                  sp[e0 + 3], sp[e0 + 4], sp[e0 + 5],
-                                  sp[e0 + 6], sp[e0 + 7]);
-      const bf16_t *vr = Vs + (16 * ks + trow) * KP + tcol;
-#pragma unroll
-      for (int db = 0; db < Dm::DB; ++db) {
-        const bf16x4 lo = lds_read_tr(vr + 32 * db);
-        const bf16x4 hi = lds_read_tr(vr + 8 * KP + 32 * db);
-        oacc[db] = mfma32(cat4(lo, hi), pb, oacc[db]);
+        for (int db = 0; db < Dm::DB; ++db) {
+          const bf16x4 lo = lds_read_tr(vr + 32 * db);
+          const bf16x4 hi = lds_read_tr(vr + 8 * KP + 32 * db);
+          oacc[db] = mfma32(cat4(lo, hi), pb, oacc[db]);
+        }
       }
     }
+    if (more) stage(buf ^ 1);
+    __syncthreads();
   }
 
   // Epilogue: normalise, write O and LSE at the original position.
@@ -236,7 +279,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void s2a_fwd_kernel(
       }
     if (hf == 0)
       lse[((size_t)b * p.H + h) * N + qpos] =
-          qvalid ? (m_run + __builtin_amdgcn_logf(lt)) * S2A_LN2 : -INFINITY;
+          qvalid ? (m_ref + __builtin_amdgcn_logf(lt)) * S2A_LN2 : -INFINITY;
   }
 }
 
