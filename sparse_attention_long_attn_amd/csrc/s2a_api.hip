@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/s2attn.h"
+#include "s2attn.h"
 #include "s2a_device.h"
 #include "s2a_kernels.h"
 
