@@ -138,19 +138,22 @@ def main():
         s2a.fwd(q, k, v, o=o, lse=lse, **kw)
         if ev is not None:
             ev[1].record()
-        s2a.bwd_preprocess(o, do, dq, delta)
+        s2a.bwd_preprocess(o, do, delta)
         if ev is not None:
             ev[2].record()
-        s2a.bwd_main(q, k, v, lse, delta, do, dq, dk, dv, **kw)
+        s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
         if ev is not None:
             ev[3].record()
+        s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+        if ev is not None:
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
            for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -164,15 +167,21 @@ def main():
     ms_step = total_ms / K
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     pre_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
-    main_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    dkdv_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    dq_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / K
 
     f_fwd, f_bwd = work.useful_flops(B, N, H, D, G, shift, bnd, L)
     b_fwd, b_bwd = work.algorithmic_bytes(B, N, H, D, o_bytes=4)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
+    # useful work of each kernel: QK^T and PV (fwd); the backward's 10*D
+    # per pair is dV, dK, dP and S in the dK/dV kernel (8*D) and dQ (2*D)
+    # in the dQ kernel, which also recomputes S and dP (not counted)
+    D_pairs = f_fwd // (4 * D)
     kernels = {
         "s2a_fwd_kernel": (fwd_ms, f_fwd),
-        "s2a_bwd_kernel": (main_ms, f_bwd),
+        "s2a_bwd_dkdv_kernel": (dkdv_ms, 8 * D * D_pairs),
+        "s2a_bwd_dq_kernel": (dq_ms, 2 * D * D_pairs),
     }
     dom = max(kernels, key=lambda n: kernels[n][0])
     dms, dfl = kernels[dom]
@@ -208,9 +217,11 @@ def main():
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_preprocess_ms": round(pre_ms, 4),
-        "bwd_main_ms": round(main_ms, 4),
+        "bwd_dkdv_ms": round(dkdv_ms, 4),
+        "bwd_dq_ms": round(dq_ms, 4),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / ((pre_ms + main_ms) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((pre_ms + dkdv_ms + dq_ms) * 1e-3) / 1e12,
+                            2),
         "useful_flops_per_step": f_fwd + f_bwd,
         "algorithmic_bytes": {"fwd": b_fwd, "bwd": b_bwd},
         "roofline": roofline,

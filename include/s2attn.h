@@ -91,8 +91,8 @@ s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
  * of dq, dk and dv are exactly 0.
  *
  * delta_ws: caller-provided f32 workspace of B*H*N floats; on return it
- * holds delta_x.  dq is accumulated with device atomics, so its last bits
- * may differ between runs; dk and dv are deterministic.
+ * holds delta_x.  Every output element is written exactly once (no
+ * atomics), so results are bitwise repeatable.
  */
 s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       const void *o, int o_dtype, const float *lse,
@@ -102,23 +102,31 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       void *stream);
 
 /*
- * The two stages of s2attn_bwd, for callers that schedule or time them
- * separately.  s2attn_bwd_preprocess writes delta_ws[b,h,x] = dout[x].o[x]
- * and clears dq; s2attn_bwd_main then accumulates dq and writes dk, dv.
- * Calling both in this order on one stream equals s2attn_bwd.  Arguments,
- * layouts and checks are those of s2attn_bwd.
+ * The three stages of s2attn_bwd, for callers that schedule or time them
+ * separately.  Calling them in this order on one stream equals s2attn_bwd;
+ * the last two only read delta_ws and may run in either order or
+ * concurrently once it is written.
+ *   s2attn_bwd_preprocess  delta_ws[b,h,x] = dout[x].o[x]
+ *   s2attn_bwd_dkdv        writes dk and dv (every row)
+ *   s2attn_bwd_dq          writes dq (every row)
+ * Arguments, layouts and checks are those of s2attn_bwd.
  */
 s2a_status s2attn_bwd_preprocess(const void *o, int o_dtype,
-                                 const void *dout, float *dq,
-                                 float *delta_ws, int B, int N, int H, int D,
-                                 void *stream);
+                                 const void *dout, float *delta_ws, int B,
+                                 int N, int H, int D, void *stream);
 
-s2a_status s2attn_bwd_main(const void *q, const void *k, const void *v,
+s2a_status s2attn_bwd_dkdv(const void *q, const void *k, const void *v,
                            const float *lse, const float *delta_ws,
-                           const void *dout, float *dq, float *dk, float *dv,
-                           int B, int N, int H, int D, int G, int shift,
+                           const void *dout, float *dk, float *dv, int B,
+                           int N, int H, int D, int G, int shift,
                            int boundary, int valid_len, float scale,
                            void *stream);
+
+s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
+                         const float *lse, const float *delta_ws,
+                         const void *dout, float *dq, int B, int N, int H,
+                         int D, int G, int shift, int boundary,
+                         int valid_len, float scale, void *stream);
 
 /*
  * Group index maps, computed on the device by the same group geometry the

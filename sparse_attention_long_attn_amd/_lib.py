@@ -17,8 +17,8 @@ S2A_WRAP, S2A_SPLIT = 0, 1
 S2A_BF16, S2A_F32 = 0, 1
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
-           "s2attn_bwd_main", "s2attn_group_map", "s2attn_strerror",
-           "s2attn_last_error", "s2attn_version")
+           "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_group_map",
+           "s2attn_strerror", "s2attn_last_error", "s2attn_version")
 
 _lib = None
 
@@ -43,11 +43,14 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
                                I, I, I, I, I, I, I, I, F, P]
     lib.s2attn_bwd.restype = I
-    lib.s2attn_bwd_preprocess.argtypes = [P, I, P, P, P, I, I, I, I, P]
+    lib.s2attn_bwd_preprocess.argtypes = [P, I, P, P, I, I, I, I, P]
     lib.s2attn_bwd_preprocess.restype = I
-    lib.s2attn_bwd_main.argtypes = [P, P, P, P, P, P, P, P, P,
+    lib.s2attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P,
                                     I, I, I, I, I, I, I, I, F, P]
-    lib.s2attn_bwd_main.restype = I
+    lib.s2attn_bwd_dkdv.restype = I
+    lib.s2attn_bwd_dq.argtypes = [P, P, P, P, P, P, P,
+                                  I, I, I, I, I, I, I, I, F, P]
+    lib.s2attn_bwd_dq.restype = I
     lib.s2attn_group_map.argtypes = [I, I, I, I, I, P, P, P, P]
     lib.s2attn_group_map.restype = I
     lib.s2attn_strerror.argtypes = [I]

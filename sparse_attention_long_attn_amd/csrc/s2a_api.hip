@@ -79,6 +79,25 @@ s2a_status hip_status(hipError_t e, const char *what) {
   return S2A_EHIP;
 }
 
+// Shared checks of the two gradient stages.
+s2a_status check_grad_stage(const void *q, const void *k, const void *v,
+                            const float *lse, const float *delta_ws,
+                            const void *dout, const void *o1, const void *o2,
+                            int B, int N, int H, int D, int G, int shift,
+                            int boundary, int valid_len, float scale) {
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!q || !k || !v || !lse || !delta_ws || !dout || !o1 || !o2)
+    return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) ||
+      !aligned16(delta_ws) || !aligned16(dout) || !aligned16(o1) ||
+      !aligned16(o2))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  return S2A_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,7 +145,7 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, s2a_bwd_tile_rows());
+                                  scale, 1);
   return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
                                    dq, dk, dv, delta_ws, D, p,
                                    (hipStream_t)stream),
@@ -134,49 +153,54 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
 }
 
 s2a_status s2attn_bwd_preprocess(const void *o, int o_dtype,
-                                 const void *dout, float *dq,
-                                 float *delta_ws, int B, int N, int H, int D,
-                                 void *stream) {
+                                 const void *dout, float *delta_ws, int B,
+                                 int N, int H, int D, void *stream) {
   g_err[0] = 0;
   if (B <= 0 || N <= 0 || H <= 0 || D <= 0)
     return fail(S2A_EINVAL, "sizes must be positive");
   if (D != 16 && D != 32 && D != 64 && D != 128)
     return fail(S2A_EUNSUPPORTED, "head width D=%lld not in {16,32,64,128}", D);
-  if (!o || !dout || !dq || !delta_ws)
-    return fail(S2A_EINVAL, "NULL tensor pointer");
-  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(delta_ws))
+  if (!o || !dout || !delta_ws) return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta_ws))
     return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
   if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
     return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
-  return hip_status(s2a_launch_bwd_pre(o, o_dtype == S2A_F32, dout, dq,
-                                       delta_ws, B, N, H, D,
-                                       (hipStream_t)stream),
+  return hip_status(s2a_launch_bwd_pre(o, o_dtype == S2A_F32, dout, delta_ws,
+                                       B, N, H, D, (hipStream_t)stream),
                     "backward preprocess launch");
 }
 
-s2a_status s2attn_bwd_main(const void *q, const void *k, const void *v,
+s2a_status s2attn_bwd_dkdv(const void *q, const void *k, const void *v,
                            const float *lse, const float *delta_ws,
-                           const void *dout, float *dq, float *dk, float *dv,
-                           int B, int N, int H, int D, int G, int shift,
+                           const void *dout, float *dk, float *dv, int B,
+                           int N, int H, int D, int G, int shift,
                            int boundary, int valid_len, float scale,
                            void *stream) {
   g_err[0] = 0;
-  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  s2a_status st = check_grad_stage(q, k, v, lse, delta_ws, dout, dk, dv, B, N,
+                                   H, D, G, shift, boundary, valid_len, scale);
   if (st != S2A_OK) return st;
-  if (!q || !k || !v || !lse || !delta_ws || !dout || !dq || !dk || !dv)
-    return fail(S2A_EINVAL, "NULL tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) ||
-      !aligned16(delta_ws) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv))
-    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
-  if (!(scale > 0.f) || !isfinite(scale))
-    return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, s2a_bwd_tile_rows());
-  return hip_status(s2a_launch_bwd_main(q, k, v, lse, delta_ws, dout, dq, dk,
-                                        dv, D, p, (hipStream_t)stream),
-                    "backward main launch");
+                                  scale, 1);
+  return hip_status(s2a_launch_bwd_dkdv(q, k, v, dout, lse, delta_ws, dk, dv,
+                                        D, p, (hipStream_t)stream),
+                    "dK/dV launch");
+}
+
+s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
+                         const float *lse, const float *delta_ws,
+                         const void *dout, float *dq, int B, int N, int H,
+                         int D, int G, int shift, int boundary,
+                         int valid_len, float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_grad_stage(q, k, v, lse, delta_ws, dout, dq, dq, B, N,
+                                   H, D, G, shift, boundary, valid_len, scale);
+  if (st != S2A_OK) return st;
+  const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
+                                  scale, 1);
+  return hip_status(s2a_launch_bwd_dq(q, k, v, dout, lse, delta_ws, dq, D, p,
+                                      (hipStream_t)stream),
+                    "dQ launch");
 }
 
 s2a_status s2attn_group_map(int N, int G, int shift, int boundary,

@@ -4,42 +4,61 @@
 // "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调", §3) and stay inside each
 // group: no out-of-group pair is ever visited (§1.1, "反向传播确实保持稀疏").
 //
-// s2a_bwd_pre_kernel    delta_x = dO_x . O_x per (batch, head, row), and
-//                       dQ cleared (it is accumulated with atomics)
-// s2a_bwd_kernel        one workgroup owns 128 keys of one group and walks
-//                       the group's query tiles at or after them:
-//                         S  = Q K^T,  dP = dO V^T      (MFMA, K/V in regs)
-//                         P  = exp(S - lse),  dS = P (dP - delta)
-//                         dV^T += dO^T P,  dK^T += Q^T dS  (MFMA, registers)
-//                         dQ += dS K  -> fp32 atomics at the rows' original
-//                                        positions
-//                       dK and dV are stored once at the end.
+// Three kernels, none using atomics:
+//   s2a_bwd_pre_kernel   delta_x = dO_x . O_x per (batch, head, row)
+//   s2a_bwd_dkdv_kernel  one workgroup owns 128 keys of one group and walks
+//                        the group's query tiles at or after them:
+//                          S = Q K^T, dP = dO V^T         (K, V in registers)
+//                          P = exp(S - lse), dS = P (dP - delta)
+//                          dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through
+//                                                          transposing LDS reads)
+//                        and stores dK, dV once at the end;
+//   s2a_bwd_dq_kernel    one workgroup owns 128 queries of one group and
+//                        walks the group's key tiles up to them, in the
+//                        forward's orientation (one query per lane column):
+//                          S^T = K Q^T, dP^T = V dO^T, dS^T as above,
+//                          dQ^T += K^T dS^T
+//                        and stores dQ once at the end.
+// Splitting dQ off costs 4*D extra MFMA work per pair (S and dP are
+// recomputed) but replaces fp32 atomics whose traffic (one read-modify-
+// write of a 64x128 fp32 tile per key tile and query tile) cost more than
+// the whole rest of the backward.
 #include "s2a_device.h"
 #include "s2a_kernels.h"
 
 namespace {
 
-constexpr int BWD_BK = 128;  // keys per workgroup, 32 per wave
-constexpr int BWD_BQ = 64;   // queries per inner tile
-constexpr int BWD_THREADS = 256;
+constexpr int KV_BK = 128;   // keys per dK/dV workgroup, 32 per wave
+constexpr int KV_BQ = 64;    // queries per inner tile of the dK/dV kernel
+constexpr int DQ_BQ = 128;   // queries per dQ workgroup, 32 per wave
+constexpr int DQ_BK = 64;    // keys per inner tile of the dQ kernel
+constexpr int THREADS = 256;
 
 template <int D>
 struct BwdDims {
   static constexpr int DP = D < 32 ? 32 : D;
-  static constexpr int KP = DP + 16;      // LDS row pitch of K, Q, dO tiles
-  static constexpr int SP = BWD_BQ + 8;   // LDS row pitch of dS^T
+  static constexpr int KP = DP + 16;      // LDS row pitch, elements
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = DP / 32;
-  static constexpr int CPR = DP / 8;
+  static constexpr int CPR = DP / 8;      // 16-byte chunks per row
 };
 
+// True if the slots [k0, kend) of a group hold a position >= L.
+__device__ __forceinline__ bool range_has_padding(int base, int k0, int kend,
+                                                  int N, int L) {
+  if (L >= N) return false;
+  const int first = s2a_slot_pos(base, k0, N);
+  const int last = s2a_slot_pos(base, kend - 1, N);
+  return last >= first ? last >= L : true;  // a wrapped range holds N-1
+}
+
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO * O), dQ = 0
+// delta = rowsum(dO * O)
 // ---------------------------------------------------------------------------
 template <int D, bool OF32>
 __global__ __launch_bounds__(256) void s2a_bwd_pre_kernel(
     const void *__restrict__ o, const bf16_t *__restrict__ dout,
-    float *__restrict__ delta, float *__restrict__ dq, int B, int N, int H) {
+    float *__restrict__ delta, int B, int N, int H) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const size_t rows = (size_t)B * N * H;
@@ -66,9 +85,6 @@ __global__ __launch_bounds__(256) void s2a_bwd_pre_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)g[e], ov[e], acc);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4 *)(dq + off) = z;
-    *(f32x4 *)(dq + off + 4) = z;
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -81,54 +97,67 @@ __global__ __launch_bounds__(256) void s2a_bwd_pre_kernel(
   }
 }
 
+// Workgroup -> (unit, tile) shared by the backward kernels: the tiles of a
+// (batch, head, group) unit get workgroup ids equal mod 8, so they run on
+// one XCD and share its L2.
+struct UnitTile {
+  int b, h, cls, base, glen, tile;
+  bool ok;
+};
+
+__device__ __forceinline__ UnitTile decode(const S2AParams &p, bool reverse) {
+  UnitTile r;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, jj = bid >> 3;
+  const int lu = jj / p.tiles;
+  const int t = jj - lu * p.tiles;
+  r.tile = reverse ? p.tiles - 1 - t : t;
+  const int u = lu * 8 + xcd;
+  r.ok = u < p.units;
+  if (!r.ok) return r;
+  const int gi = u % p.ngmax;
+  const int bh = u / p.ngmax;
+  r.h = bh % p.H;
+  r.b = bh / p.H;
+  r.cls = r.h >= (p.H >> 1);
+  r.ok = s2a_group(p.g, r.cls, gi, r.base, r.glen);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
-// main backward
+// dK, dV (key-outer)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
+__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ delta,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
-    S2AParams p) {
+    float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
   using Dm = BwdDims<D>;
-  constexpr int KP = Dm::KP, SP = Dm::SP;
-  constexpr int QT = BWD_BQ * KP;                        // elements per buffer
-  constexpr int NCH = BWD_BQ * Dm::CPR / BWD_THREADS;    // chunks per thread
-  static_assert(BWD_BQ * Dm::CPR % BWD_THREADS == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16_t Ksm[BWD_BK * KP];
+  constexpr int KP = Dm::KP;
+  constexpr int QT = KV_BQ * KP;                      // elements per buffer
+  constexpr int NCH = KV_BQ * Dm::CPR / THREADS;      // chunks per thread
+  static_assert(KV_BQ * Dm::CPR % THREADS == 0, "tile split");
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2 * QT];
   __shared__ __attribute__((aligned(16))) bf16_t dOs[2 * QT];
-  __shared__ __attribute__((aligned(16))) bf16_t dSt[BWD_BK * SP];
-  __shared__ __attribute__((aligned(16))) float lse2s[2 * BWD_BQ];
-  __shared__ __attribute__((aligned(16))) float dlts[2 * BWD_BQ];
+  __shared__ __attribute__((aligned(16))) float lse2s[2 * KV_BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[2 * KV_BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int grp = lane >> 4;
-  const int trow = 4 * hf + ((lane & 15) >> 2);   // tr-read row in a 16-step
+  const int trow = 4 * hf + ((lane & 15) >> 2);      // tr-read row in a step
   const int tcol = 16 * (grp & 1) + 4 * (lane & 3);  // tr-read column
 
-  // Workgroup -> (unit, key tile); all key tiles of a unit on one XCD,
-  // first key tile (longest query walk) first.
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, jj = bid >> 3;
-  const int lu = jj / p.tiles;
-  const int tile = jj - lu * p.tiles;
-  const int u = lu * 8 + xcd;
-  if (u >= p.units) return;
-  const int gi = u % p.ngmax;
-  const int bh = u / p.ngmax;
-  const int h = bh % p.H, b = bh / p.H;
-  const int cls = h >= (p.H >> 1);
-  int base, glen;
-  if (!s2a_group(p.g, cls, gi, base, glen)) return;
-  const int k0 = tile * BWD_BK;
+  const UnitTile ut = decode(p, false);  // first key tile (longest walk) first
+  if (!ut.ok) return;
+  const int base = ut.base, glen = ut.glen;
+  const int k0 = ut.tile * KV_BK;
   if (k0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
   const size_t rs = (size_t)p.H * D;
-  const size_t boff = (size_t)b * N * rs + (size_t)h * D;
-  const size_t lrow = ((size_t)b * p.H + h) * N;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
   const float c2 = p.scale_log2;
 
   // This lane's key (one column of S) and the wave's key range.
@@ -153,17 +182,6 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
       vreg[t] = __builtin_bit_cast(bf16x8, c);
     }
   }
-  // K tile in LDS (B operand of dQ = dS K).
-  for (int c = tid; c < BWD_BK * Dm::CPR; c += BWD_THREADS) {
-    const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
-    const int ks = k0 + r;
-    u32x4 kv = {0u, 0u, 0u, 0u};
-    if (ks < glen && ch * 8 < D) {
-      const int kp = s2a_slot_pos(base, ks, N);
-      if (kp < L) kv = *(const u32x4 *)(k + boff + (size_t)kp * rs + ch * 8);
-    }
-    *(u32x4 *)(Ksm + r * KP + ch * 8) = kv;
-  }
 
   // Query-tile staging through registers.  Rows outside the group or padded
   // get q = dO = 0, lse = +inf (so P = 0) and delta = 0 (so dS = 0).
@@ -172,7 +190,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
   auto fetch = [&](int q0) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * BWD_THREADS;
+      const int c = tid + i * THREADS;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       const int qsl = q0 + r;
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
@@ -187,7 +205,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
       qst[i] = qv;
       gst[i] = gv;
     }
-    if (tid < BWD_BQ) {
+    if (tid < KV_BQ) {
       const int qsl = q0 + tid;
       l2st = INFINITY;
       dlst = 0.f;
@@ -203,14 +221,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * BWD_THREADS;
+      const int c = tid + i * THREADS;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       *(u32x4 *)(Qs + buf * QT + r * KP + ch * 8) = qst[i];
       *(u32x4 *)(dOs + buf * QT + r * KP + ch * 8) = gst[i];
     }
-    if (tid < BWD_BQ) {
-      lse2s[buf * BWD_BQ + tid] = l2st;
-      dlts[buf * BWD_BQ + tid] = dlst;
+    if (tid < KV_BQ) {
+      lse2s[buf * KV_BQ + tid] = l2st;
+      dlts[buf * KV_BQ + tid] = dlst;
     }
   };
 
@@ -223,23 +241,22 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
       dvacc[db][i] = 0.f;
     }
 
-  const int nq = (glen - k0 + BWD_BQ - 1) / BWD_BQ;  // query tiles from k0
+  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;  // query tiles from k0
   fetch(k0);
   stage(0);
   __syncthreads();
 
   for (int it = 0; it < nq; ++it) {
-    const int q0 = k0 + it * BWD_BQ;
+    const int q0 = k0 + it * KV_BQ;
     const int buf = it & 1;
     const bool more = it + 1 < nq;
-    if (more) fetch(q0 + BWD_BQ);  // in flight during this tile's math
-    const bf16_t *Qb = Qs + buf * QT;
-    const bf16_t *dOb = dOs + buf * QT;
-    const float *l2b = lse2s + buf * BWD_BQ;
-    const float *dlb = dlts + buf * BWD_BQ;
+    if (more) fetch(q0 + KV_BQ);  // in flight during this tile's math
 
-    const bool active = q0 + BWD_BQ - 1 >= kw0;
-    if (active) {
+    if (q0 + KV_BQ - 1 >= kw0) {  // else all queries precede the wave's keys
+      const bf16_t *Qb = Qs + buf * QT;
+      const bf16_t *dOb = dOs + buf * QT;
+      const float *l2b = lse2s + buf * KV_BQ;
+      const float *dlb = dlts + buf * KV_BQ;
       f32x16 sacc[2], dpacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -277,7 +294,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
         }
       // dV^T += dO^T P and dK^T += Q^T dS over 64 queries (4 steps of 16).
 #pragma unroll
-      for (int qs = 0; qs < BWD_BQ / 16; ++qs) {
+      for (int qs = 0; qs < KV_BQ / 16; ++qs) {
         const int e0 = 8 * (qs & 1);
         const f32x16 &sp = sacc[qs >> 1];
         const f32x16 &dp = dpacc[qs >> 1];
@@ -296,55 +313,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
           dkacc[db] = mfma32(aq, sb, dkacc[db]);
         }
       }
-      // dS^T tile (bf16) for the dQ product.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x16 &dp = dpacc[qb];
-          *(bf16x4 *)(dSt + (32 * w + l32) * SP + 32 * qb + 8 * i4 + 4 * hf) =
-              to_bf16x4(dp[4 * i4], dp[4 * i4 + 1], dp[4 * i4 + 2], dp[4 * i4 + 3]);
-        }
-    } else {
-      const bf16x4 z = to_bf16x4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *(bf16x4 *)(dSt + (32 * w + l32) * SP + 32 * qb + 8 * i4 + 4 * hf) = z;
-    }
-    __syncthreads();  // dS^T complete
-
-    // dQ[q][d] += dS[q][key] K[key][d] over the workgroup's 128 keys.
-    for (int blk = w; blk < 2 * Dm::DB; blk += 4) {
-      const int qb = blk & 1, db = blk >> 1;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < BWD_BK / 16; ++ks) {
-        const int r = 16 * ks + trow;
-        const bf16x8 as = cat4(lds_read_tr(dSt + r * SP + 32 * qb + tcol),
-                               lds_read_tr(dSt + (r + 8) * SP + 32 * qb + tcol));
-        const bf16x8 bk = cat4(lds_read_tr(Ksm + r * KP + 32 * db + tcol),
-                               lds_read_tr(Ksm + (r + 8) * KP + 32 * db + tcol));
-        acc = mfma32(as, bk, acc);
-      }
-      const int d = 32 * db + l32;
-      if (d < D) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qsl = q0 + 32 * qb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (qsl < glen) {
-            const int qp = s2a_slot_pos(base, qsl, N);
-            if (qp < L)
-              unsafeAtomicAdd(dq + boff + (size_t)qp * rs + d, acc[i] * p.scale);
-          }
-        }
-      }
     }
     if (more) stage(buf ^ 1);
-    __syncthreads();  // next tile staged; dS^T reads done
+    __syncthreads();
   }
 
   // dK, dV rows of this lane's key (padded keys get their exact zeros).
@@ -367,48 +338,248 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void s2a_bwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ (query-outer)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ delta,
+    float *__restrict__ dq, S2AParams p) {
+  using Dm = BwdDims<D>;
+  constexpr int KP = Dm::KP;
+  constexpr int TILE = DQ_BK * KP;
+  constexpr int NCH = DQ_BK * Dm::CPR / THREADS;
+  static_assert(DQ_BK * Dm::CPR % THREADS == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+  const int tcol = 16 * (grp & 1) + 4 * (lane & 3);
+
+  const UnitTile ut = decode(p, true);  // heaviest (last) query tile first
+  if (!ut.ok) return;
+  const int base = ut.base, glen = ut.glen;
+  const int q0 = ut.tile * DQ_BQ;
+  if (q0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
+  const float c2 = p.scale_log2;
+
+  // This lane's query (one column of S^T, dP^T, dS^T).
+  const int qslot = q0 + 32 * w + l32;
+  const bool qin = qslot < glen;
+  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const bool qvalid = qin && qpos < L;
+  const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
+  const float dl = qvalid ? delta[lrow + qpos] : 0.f;
+
+  bf16x8 qreg[Dm::KSTEPS], greg[Dm::KSTEPS];
+  {
+    const size_t off = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int t = 0; t < Dm::KSTEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (qvalid) {
+        a = *(const u32x4 *)(q + off + 16 * t + 8 * hf);
+        c = *(const u32x4 *)(dout + off + 16 * t + 8 * hf);
+      }
+      qreg[t] = __builtin_bit_cast(bf16x8, a);
+      greg[t] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+
+  u32x4 kst[NCH], vst[NCH];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * THREADS;
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      const int ks = k0 + r;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (ks < glen && ch * 8 < D) {
+        const int kp = s2a_slot_pos(base, ks, N);
+        if (kp < L) {
+          const size_t off = boff + (size_t)kp * rs + ch * 8;
+          kv = *(const u32x4 *)(k + off);
+          vv = *(const u32x4 *)(v + off);
+        }
+      }
+      kst[i] = kv;
+      vst[i] = vv;
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * THREADS;
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      *(u32x4 *)(Ks + buf * TILE + r * KP + ch * 8) = kst[i];
+      *(u32x4 *)(Vs + buf * TILE + r * KP + ch * 8) = vst[i];
+    }
+  };
+
+  f32x16 dqacc[Dm::DB];
+#pragma unroll
+  for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  const int kend = min(glen, q0 + DQ_BQ);
+  const int ntiles = (kend + DQ_BK - 1) / DQ_BK;
+  const int wq_lo = q0 + 32 * w;
+  const int wq_hi = wq_lo + 31;
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * DQ_BK;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) fetch(k0 + DQ_BK);
+
+    if (k0 <= wq_hi) {
+      const bf16_t *Kb = Ks + buf * TILE;
+      const bf16_t *Vb = Vs + buf * TILE;
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[kb][i] = 0.f;
+          dpacc[kb][i] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < Dm::KSTEPS; ++t) {
+          const int ro = (32 * kb + l32) * KP + 16 * t + 8 * hf;
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Kb + ro));
+          const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vb + ro));
+          sacc[kb] = mfma32(ak, qreg[t], sacc[kb]);
+          dpacc[kb] = mfma32(av, greg[t], dpacc[kb]);
+        }
+      }
+      // dS^T; element i of block kb is key k0 + 32kb + 8(i/4) + 4hf + i%4.
+      const int kstop = min(k0 + DQ_BK, glen);
+      const bool edge = (k0 + DQ_BK - 1 > wq_lo) || (k0 + DQ_BK > glen) ||
+                        range_has_padding(base, k0, kstop, N, L);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
+          if (edge) {
+            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (!(ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L))
+              pp = 0.f;
+          }
+          dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
+        }
+      // dQ^T += K^T dS^T, 16 keys per MFMA (same key order on both sides).
+#pragma unroll
+      for (int ks = 0; ks < DQ_BK / 16; ++ks) {
+        const f32x16 &dp = dpacc[ks >> 1];
+        const int e0 = 8 * (ks & 1);
+        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
+                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+        const bf16_t *kr = Kb + (16 * ks + trow) * KP + tcol;
+#pragma unroll
+        for (int db = 0; db < Dm::DB; ++db) {
+          const bf16x8 ak = cat4(lds_read_tr(kr + 32 * db),
+                                 lds_read_tr(kr + 8 * KP + 32 * db));
+          dqacc[db] = mfma32(ak, sb, dqacc[db]);
+        }
+      }
+    }
+    if (more) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qin) {
+    const size_t row = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        if (d < D) {
+          f32x4 val = {0.f, 0.f, 0.f, 0.f};
+          if (qvalid) {
+            val[0] = dqacc[db][4 * i4] * p.scale;
+            val[1] = dqacc[db][4 * i4 + 1] * p.scale;
+            val[2] = dqacc[db][4 * i4 + 2] * p.scale;
+            val[3] = dqacc[db][4 * i4 + 3] * p.scale;
+          }
+          *(f32x4 *)(dq + row + d) = val;
+        }
+      }
+  }
+}
+
 template <int D, bool OF32>
-hipError_t launch_pre_t(const void *o, const void *dout, float *delta,
-                        float *dq, int B, int N, int H, hipStream_t st) {
+hipError_t launch_pre_t(const void *o, const void *dout, float *delta, int B,
+                        int N, int H, hipStream_t st) {
   constexpr int RPB = 256 / (D / 8);
   const size_t rows = (size_t)B * N * H;
   dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
   const bf16_t *g = (const bf16_t *)dout;
-  void *args[] = {(void *)&o, (void *)&g, (void *)&delta, (void *)&dq,
-                  (void *)&B, (void *)&N, (void *)&H};
+  void *args[] = {(void *)&o, (void *)&g, (void *)&delta, (void *)&B,
+                  (void *)&N, (void *)&H};
   return hipLaunchKernel((const void *)s2a_bwd_pre_kernel<D, OF32>, grid,
                          block, args, 0, st);
 }
 
-template <int D>
-hipError_t launch_bwd_t(const void *q, const void *k, const void *v,
-                        const void *dout, const float *lse, const float *delta,
-                        float *dq, float *dk, float *dv, const S2AParams &p,
-                        hipStream_t st) {
+dim3 unit_grid(const S2AParams &p, int rows_per_wg) {
   const int units_pad = (p.units + 7) / 8 * 8;
-  dim3 grid((unsigned)units_pad * (unsigned)p.tiles), block(BWD_THREADS);
+  const int tiles = (p.g.G + rows_per_wg - 1) / rows_per_wg;
+  return dim3((unsigned)units_pad * (unsigned)tiles);
+}
+
+template <int D>
+hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
+                         const void *dout, const float *lse,
+                         const float *delta, float *dk, float *dv,
+                         S2AParams p, hipStream_t st) {
+  p.tiles = (p.g.G + KV_BK - 1) / KV_BK;
   const bf16_t *qq = (const bf16_t *)q, *kk = (const bf16_t *)k,
                *vv = (const bf16_t *)v, *gg = (const bf16_t *)dout;
-  S2AParams pp = p;
-  void *args[] = {(void *)&qq,  (void *)&kk, (void *)&vv, (void *)&gg,
-                  (void *)&lse, (void *)&delta, (void *)&dq, (void *)&dk,
-                  (void *)&dv,  (void *)&pp};
-  return hipLaunchKernel((const void *)s2a_bwd_kernel<D>, grid, block, args,
-                         0, st);
+  void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
+                  (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
+                  (void *)&p};
+  return hipLaunchKernel((const void *)s2a_bwd_dkdv_kernel<D>,
+                         unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+}
+
+template <int D>
+hipError_t launch_dq_t(const void *q, const void *k, const void *v,
+                       const void *dout, const float *lse, const float *delta,
+                       float *dq, S2AParams p, hipStream_t st) {
+  p.tiles = (p.g.G + DQ_BQ - 1) / DQ_BQ;
+  const bf16_t *qq = (const bf16_t *)q, *kk = (const bf16_t *)k,
+               *vv = (const bf16_t *)v, *gg = (const bf16_t *)dout;
+  void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
+                  (void *)&lse, (void *)&delta, (void *)&dq, (void *)&p};
+  return hipLaunchKernel((const void *)s2a_bwd_dq_kernel<D>,
+                         unit_grid(p, DQ_BQ), dim3(THREADS), args, 0, st);
 }
 
 }  // namespace
 
-int s2a_bwd_tile_rows() { return BWD_BK; }
-
 hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
-                              float *dq, float *delta, int B, int N, int H,
-                              int D, hipStream_t st) {
+                              float *delta, int B, int N, int H, int D,
+                              hipStream_t st) {
   switch (D) {
-#define S2A_CASE(DD)                                                       \
-  case DD:                                                                 \
-    return o_f32 ? launch_pre_t<DD, true>(o, dout, delta, dq, B, N, H, st)  \
-                 : launch_pre_t<DD, false>(o, dout, delta, dq, B, N, H, st);
+#define S2A_CASE(DD)                                                      \
+  case DD:                                                                \
+    return o_f32 ? launch_pre_t<DD, true>(o, dout, delta, B, N, H, st)    \
+                 : launch_pre_t<DD, false>(o, dout, delta, B, N, H, st);
     S2A_CASE(16)
     S2A_CASE(32)
     S2A_CASE(64)
@@ -418,16 +589,28 @@ hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
   }
 }
 
-hipError_t s2a_launch_bwd_main(const void *q, const void *k, const void *v,
-                               const float *lse, const float *delta,
-                               const void *dout, float *dq, float *dk,
-                               float *dv, int D, const S2AParams &p,
-                               hipStream_t st) {
+hipError_t s2a_launch_bwd_dkdv(const void *q, const void *k, const void *v,
+                               const void *dout, const float *lse,
+                               const float *delta, float *dk, float *dv,
+                               int D, const S2AParams &p, hipStream_t st) {
   switch (D) {
-    case 16: return launch_bwd_t<16>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
-    case 32: return launch_bwd_t<32>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
-    case 64: return launch_bwd_t<64>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
-    case 128: return launch_bwd_t<128>(q, k, v, dout, lse, delta, dq, dk, dv, p, st);
+    case 16: return launch_dkdv_t<16>(q, k, v, dout, lse, delta, dk, dv, p, st);
+    case 32: return launch_dkdv_t<32>(q, k, v, dout, lse, delta, dk, dv, p, st);
+    case 64: return launch_dkdv_t<64>(q, k, v, dout, lse, delta, dk, dv, p, st);
+    case 128: return launch_dkdv_t<128>(q, k, v, dout, lse, delta, dk, dv, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t s2a_launch_bwd_dq(const void *q, const void *k, const void *v,
+                             const void *dout, const float *lse,
+                             const float *delta, float *dq, int D,
+                             const S2AParams &p, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_dq_t<16>(q, k, v, dout, lse, delta, dq, p, st);
+    case 32: return launch_dq_t<32>(q, k, v, dout, lse, delta, dq, p, st);
+    case 64: return launch_dq_t<64>(q, k, v, dout, lse, delta, dq, p, st);
+    case 128: return launch_dq_t<128>(q, k, v, dout, lse, delta, dq, p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -437,8 +620,9 @@ hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
                           const void *dout, float *dq, float *dk, float *dv,
                           float *delta, int D, const S2AParams &p,
                           hipStream_t st) {
-  const hipError_t e =
-      s2a_launch_bwd_pre(o, o_f32, dout, dq, delta, p.B, p.g.N, p.H, D, st);
+  hipError_t e = s2a_launch_bwd_pre(o, o_f32, dout, delta, p.B, p.g.N, p.H, D, st);
   if (e != hipSuccess) return e;
-  return s2a_launch_bwd_main(q, k, v, lse, delta, dout, dq, dk, dv, D, p, st);
+  e = s2a_launch_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, D, p, st);
+  if (e != hipSuccess) return e;
+  return s2a_launch_bwd_dq(q, k, v, dout, lse, delta, dq, D, p, st);
 }

@@ -7,7 +7,6 @@
 struct S2AParams;
 
 int s2a_fwd_tile_rows();  // query rows per forward workgroup
-int s2a_bwd_tile_rows();  // key rows per backward workgroup
 
 hipError_t s2a_launch_fwd(const void *q, const void *k, const void *v,
                           void *o, bool o_f32, float *lse, int D,
@@ -20,14 +19,18 @@ hipError_t s2a_launch_bwd(const void *q, const void *k, const void *v,
                           hipStream_t st);
 
 hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
-                              float *dq, float *delta, int B, int N, int H,
-                              int D, hipStream_t st);
+                              float *delta, int B, int N, int H, int D,
+                              hipStream_t st);
 
-hipError_t s2a_launch_bwd_main(const void *q, const void *k, const void *v,
-                               const float *lse, const float *delta,
-                               const void *dout, float *dq, float *dk,
-                               float *dv, int D, const S2AParams &p,
-                               hipStream_t st);
+hipError_t s2a_launch_bwd_dkdv(const void *q, const void *k, const void *v,
+                               const void *dout, const float *lse,
+                               const float *delta, float *dk, float *dv,
+                               int D, const S2AParams &p, hipStream_t st);
+
+hipError_t s2a_launch_bwd_dq(const void *q, const void *k, const void *v,
+                             const void *dout, const float *lse,
+                             const float *delta, float *dq, int D,
+                             const S2AParams &p, hipStream_t st);
 
 hipError_t s2a_launch_map(const S2AGeom &g, int *gid, int *slot, int *src,
                           hipStream_t st);

@@ -108,31 +108,51 @@ def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
     return dq, dk, dv
 
 
-def bwd_preprocess(o, dout, dq, delta):
-    """First backward stage: delta = rowsum(dout * o), dq = 0."""
+def bwd_preprocess(o, dout, delta):
+    """First backward stage: delta = rowsum(dout * o)."""
     B, N, H, D = _check_qkv(dout)
     odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()
-    _lib.check(lib.s2attn_bwd_preprocess(_ptr(o), odt, _ptr(dout), _ptr(dq),
+    _lib.check(lib.s2attn_bwd_preprocess(_ptr(o), odt, _ptr(dout),
                                          _ptr(delta), B, N, H, D,
                                          _stream(dout.device)))
 
 
-def bwd_main(q, k, v, lse, delta, dout, dq, dk, dv, *, G: int,
-             shift: int | None = None, boundary="wrap",
-             valid_len: int | None = None, scale: float | None = None):
-    """Second backward stage: accumulates dq (cleared by bwd_preprocess),
-    writes dk and dv."""
-    B, N, H, D = _check_qkv(q, k, v, dout)
+def _stage_args(q, G, shift, valid_len, scale):
+    B, N, H, D = q.shape
     shift = G // 2 if shift is None else shift
     valid_len = N if valid_len is None else valid_len
     scale = 1.0 / math.sqrt(D) if scale is None else scale
+    return B, N, H, D, G, shift, valid_len, scale
+
+
+def bwd_dkdv(q, k, v, lse, delta, dout, dk, dv, *, G: int,
+             shift: int | None = None, boundary="wrap",
+             valid_len: int | None = None, scale: float | None = None):
+    """dK/dV stage (needs delta from bwd_preprocess)."""
+    _check_qkv(q, k, v, dout)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
+                                                         valid_len, scale)
     lib = _lib.load()
-    _lib.check(lib.s2attn_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
-                                   _ptr(delta), _ptr(dout), _ptr(dq),
-                                   _ptr(dk), _ptr(dv), B, N, H, D, G, shift,
+    _lib.check(lib.s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
+                                   _ptr(delta), _ptr(dout), _ptr(dk),
+                                   _ptr(dv), B, N, H, D, G, shift,
                                    _boundary(boundary), valid_len, scale,
                                    _stream(q.device)))
+
+
+def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
+           shift: int | None = None, boundary="wrap",
+           valid_len: int | None = None, scale: float | None = None):
+    """dQ stage (needs delta from bwd_preprocess)."""
+    _check_qkv(q, k, v, dout)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
+                                                         valid_len, scale)
+    lib = _lib.load()
+    _lib.check(lib.s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
+                                 _ptr(delta), _ptr(dout), _ptr(dq), B, N, H,
+                                 D, G, shift, _boundary(boundary), valid_len,
+                                 scale, _stream(q.device)))
 
 
 def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
