@@ -25,6 +25,7 @@
 // the whole rest of the backward.
 #include "s2a_device.h"
 #include "s2a_kernels.h"
+#include "s2a_tile.h"
 
 namespace {
 
@@ -523,6 +524,388 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
   }
 }
 
+// dQ for D in {64, 128}: K/V tiles in the swizzled layout of s2a_tile.h,
+// filled by direct global -> LDS loads.
+template <int D>
+__global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ delta,
+    float *__restrict__ dq, S2AParams p) {
+  using T = SwTile<D>;
+  using LD = TileLoader<D, DQ_BK, THREADS / 64>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  constexpr int TILEB = DQ_BK * T::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  char *const Ks = smem;
+  char *const Vs = smem + 2 * TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+
+  const UnitTile ut = decode(p, true);
+  if (!ut.ok) return;
+  const int base = ut.base, glen = ut.glen;
+  const int q0 = ut.tile * DQ_BQ;
+  if (q0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
+  const bf16_t *kbh = k + boff, *vbh = v + boff;
+  const float c2 = p.scale_log2;
+
+  const int qslot = q0 + 32 * w + l32;
+  const bool qin = qslot < glen;
+  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const bool qvalid = qin && qpos < L;
+  const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
+  const float dl = qvalid ? delta[lrow + qpos] : 0.f;
+
+  bf16x8 qreg[KSTEPS], greg[KSTEPS];
+  {
+    const size_t off = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (qvalid) {
+        a = *(const u32x4 *)(q + off + 16 * t + 8 * hf);
+        c = *(const u32x4 *)(dout + off + 16 * t + 8 * hf);
+      }
+      qreg[t] = __builtin_bit_cast(bf16x8, a);
+      greg[t] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+
+  LD ld;
+  ld.init(w, lane);
+  auto issue = [&](int k0, int buf) {
+    char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
+    if (tile_plain(base, glen, k0, DQ_BK, N, L)) {
+      const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
+      ld.fast(kbh + r0, rs, kd);
+      ld.fast(vbh + r0, rs, vd);
+    } else {
+      ld.general(kbh, rs, base, glen, k0, N, L, kd);
+      ld.general(vbh, rs, base, glen, k0, N, L, vd);
+    }
+  };
+  int aoff[KSTEPS], troff[DB];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) aoff[t] = T::off(l32, 2 * t + hf);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    troff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
+                (lane & 1) * 8;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  const int kend = min(glen, q0 + DQ_BQ);
+  const int ntiles = (kend + DQ_BK - 1) / DQ_BK;
+  const int wq_lo = q0 + 32 * w;
+  const int wq_hi = wq_lo + 31;
+
+  issue(0, 0);
+  wait_vm_all();
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * DQ_BK;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) issue(k0 + DQ_BK, buf ^ 1);
+
+    if (k0 <= wq_hi) {
+      const char *Kb = Ks + buf * TILEB;
+      const char *Vb = Vs + buf * TILEB;
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 ak[KSTEPS], av[KSTEPS];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          ak[t] = *(const bf16x8 *)(Kb + kb * 32 * T::ROWB + aoff[t]);
+          av[t] = *(const bf16x8 *)(Vb + kb * 32 * T::ROWB + aoff[t]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[kb][i] = 0.f;
+          dpacc[kb][i] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          sacc[kb] = mfma32(ak[t], qreg[t], sacc[kb]);
+          dpacc[kb] = mfma32(av[t], greg[t], dpacc[kb]);
+        }
+      }
+      const bool edge = (k0 + DQ_BK - 1 > wq_lo) ||
+                        !tile_plain(base, glen, k0, DQ_BK, N, L);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
+          if (edge) {
+            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (!(ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L))
+              pp = 0.f;
+          }
+          dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
+        }
+#pragma unroll
+      for (int ks = 0; ks < DQ_BK / 16; ++ks) {
+        const f32x16 &dp = dpacc[ks >> 1];
+        const int e0 = 8 * (ks & 1);
+        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
+                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+        const char *kr = Kb + 16 * ks * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ak = cat4(
+              lds_read_tr((const bf16_t *)(kr + troff[db])),
+              lds_read_tr((const bf16_t *)(kr + 8 * T::ROWB + troff[db])));
+          dqacc[db] = mfma32(ak, sb, dqacc[db]);
+        }
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  if (qin) {
+    const size_t row = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
+        if (qvalid) {
+          val[0] = dqacc[db][4 * i4] * p.scale;
+          val[1] = dqacc[db][4 * i4 + 1] * p.scale;
+          val[2] = dqacc[db][4 * i4 + 2] * p.scale;
+          val[3] = dqacc[db][4 * i4 + 3] * p.scale;
+        }
+        *(f32x4 *)(dq + row + d) = val;
+      }
+  }
+}
+
+// dK/dV for D in {64, 128}: Q/dO tiles in the swizzled layout of
+// s2a_tile.h, filled by direct global -> LDS loads.
+template <int D>
+__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ delta,
+    float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
+  using T = SwTile<D>;
+  using LD = TileLoader<D, KV_BQ, THREADS / 64>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  constexpr int TILEB = KV_BQ * T::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(16))) float lse2s[2 * KV_BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[2 * KV_BQ];
+  char *const Qs = smem;
+  char *const dOs = smem + 2 * TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+
+  const UnitTile ut = decode(p, false);
+  if (!ut.ok) return;
+  const int base = ut.base, glen = ut.glen;
+  const int k0 = ut.tile * KV_BK;
+  if (k0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
+  const bf16_t *qbh = q + boff, *gbh = dout + boff;
+  const float c2 = p.scale_log2;
+
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+  const bool kin = key < glen;
+  const int kpos = kin ? s2a_slot_pos(base, key, N) : 0;
+  const bool kvalid = kin && kpos < L;
+  const bool wave_keys_valid = __all(kvalid);
+
+  bf16x8 kreg[KSTEPS], vreg[KSTEPS];
+  {
+    const size_t off = boff + (size_t)kpos * rs;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (kvalid) {
+        a = *(const u32x4 *)(k + off + 16 * t + 8 * hf);
+        c = *(const u32x4 *)(v + off + 16 * t + 8 * hf);
+      }
+      kreg[t] = __builtin_bit_cast(bf16x8, a);
+      vreg[t] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+
+  LD ld;
+  ld.init(w, lane);
+  float l2st = INFINITY, dlst = 0.f;
+  auto issue = [&](int q0, int buf) {
+    char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
+    if (tile_plain(base, glen, q0, KV_BQ, N, L)) {
+      const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
+      ld.fast(qbh + r0, rs, qd);
+      ld.fast(gbh + r0, rs, gd);
+    } else {
+      ld.general(qbh, rs, base, glen, q0, N, L, qd);
+      ld.general(gbh, rs, base, glen, q0, N, L, gd);
+    }
+    // rows outside the group or padded: lse = +inf (P = 0), delta = 0
+    if (tid < KV_BQ) {
+      const int qsl = q0 + tid;
+      l2st = INFINITY;
+      dlst = 0.f;
+      if (qsl < glen) {
+        const int qp = s2a_slot_pos(base, qsl, N);
+        if (qp < L) {
+          l2st = lse[lrow + qp] * S2A_LOG2E;
+          dlst = delta[lrow + qp];
+        }
+      }
+    }
+  };
+  auto stage_stats = [&](int buf) {
+    if (tid < KV_BQ) {
+      lse2s[buf * KV_BQ + tid] = l2st;
+      dlts[buf * KV_BQ + tid] = dlst;
+    }
+  };
+  int aoff[KSTEPS], troff[DB];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) aoff[t] = T::off(l32, 2 * t + hf);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    troff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
+                (lane & 1) * 8;
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
+  issue(k0, 0);
+  stage_stats(0);
+  wait_vm_all();
+  __syncthreads();
+
+  for (int it = 0; it < nq; ++it) {
+    const int q0 = k0 + it * KV_BQ;
+    const int buf = it & 1;
+    const bool more = it + 1 < nq;
+    if (more) issue(q0 + KV_BQ, buf ^ 1);
+
+    if (q0 + KV_BQ - 1 >= kw0) {
+      const char *Qb = Qs + buf * TILEB;
+      const char *dOb = dOs + buf * TILEB;
+      const float *l2b = lse2s + buf * KV_BQ;
+      const float *dlb = dlts + buf * KV_BQ;
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 aq[KSTEPS], ag[KSTEPS];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          aq[t] = *(const bf16x8 *)(Qb + qb * 32 * T::ROWB + aoff[t]);
+          ag[t] = *(const bf16x8 *)(dOb + qb * 32 * T::ROWB + aoff[t]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sacc[qb][i] = 0.f;
+          dpacc[qb][i] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          sacc[qb] = mfma32(aq[t], kreg[t], sacc[qb]);
+          dpacc[qb] = mfma32(ag[t], vreg[t], dpacc[qb]);
+        }
+      }
+      const bool edge = (q0 < kw0 + 31) || !wave_keys_valid;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = 32 * qb + 8 * i4 + 4 * hf;
+          const f32x4 l2 = *(const f32x4 *)(l2b + r0);
+          const f32x4 dl = *(const f32x4 *)(dlb + r0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c2, -l2[e]));
+            if (edge && !(kvalid && key <= q0 + r0 + e)) pp = 0.f;
+            dpacc[qb][i] = pp * (dpacc[qb][i] - dl[e]);
+            sacc[qb][i] = pp;
+          }
+        }
+#pragma unroll
+      for (int qs = 0; qs < KV_BQ / 16; ++qs) {
+        const int e0 = 8 * (qs & 1);
+        const f32x16 &sp = sacc[qs >> 1];
+        const f32x16 &dp = dpacc[qs >> 1];
+        const bf16x8 pb = to_bf16x8(sp[e0], sp[e0 + 1], sp[e0 + 2], sp[e0 + 3],
+                                    sp[e0 + 4], sp[e0 + 5], sp[e0 + 6], sp[e0 + 7]);
+        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
+                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+        const char *gr = dOb + 16 * qs * T::ROWB;
+        const char *qr = Qb + 16 * qs * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ag = cat4(
+              lds_read_tr((const bf16_t *)(gr + troff[db])),
+              lds_read_tr((const bf16_t *)(gr + 8 * T::ROWB + troff[db])));
+          dvacc[db] = mfma32(ag, pb, dvacc[db]);
+          const bf16x8 aq = cat4(
+              lds_read_tr((const bf16_t *)(qr + troff[db])),
+              lds_read_tr((const bf16_t *)(qr + 8 * T::ROWB + troff[db])));
+          dkacc[db] = mfma32(aq, sb, dkacc[db]);
+        }
+      }
+    }
+    if (more) stage_stats(buf ^ 1);
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  if (kin) {
+    const size_t row = boff + (size_t)kpos * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        const f32x4 kk = {dkacc[db][4 * i4] * p.scale, dkacc[db][4 * i4 + 1] * p.scale,
+                          dkacc[db][4 * i4 + 2] * p.scale, dkacc[db][4 * i4 + 3] * p.scale};
+        const f32x4 vv = {dvacc[db][4 * i4], dvacc[db][4 * i4 + 1],
+                          dvacc[db][4 * i4 + 2], dvacc[db][4 * i4 + 3]};
+        *(f32x4 *)(dk + row + d) = kk;
+        *(f32x4 *)(dv + row + d) = vv;
+      }
+  }
+}
+
 template <int D, bool OF32>
 hipError_t launch_pre_t(const void *o, const void *dout, float *delta, int B,
                         int N, int H, hipStream_t st) {
@@ -553,8 +936,10 @@ hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
   void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
                   (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
                   (void *)&p};
-  return hipLaunchKernel((const void *)s2a_bwd_dkdv_kernel<D>,
-                         unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+  const void *fn = D >= 64
+                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64)>
+                       : (const void *)s2a_bwd_dkdv_kernel<D>;
+  return hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
 }
 
 template <int D>
@@ -566,8 +951,10 @@ hipError_t launch_dq_t(const void *q, const void *k, const void *v,
                *vv = (const bf16_t *)v, *gg = (const bf16_t *)dout;
   void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
                   (void *)&lse, (void *)&delta, (void *)&dq, (void *)&p};
-  return hipLaunchKernel((const void *)s2a_bwd_dq_kernel<D>,
-                         unit_grid(p, DQ_BQ), dim3(THREADS), args, 0, st);
+  const void *fn = D >= 64
+                       ? (const void *)s2a_bwd_dq_sw_kernel<(D >= 64 ? D : 64)>
+                       : (const void *)s2a_bwd_dq_kernel<D>;
+  return hipLaunchKernel(fn, unit_grid(p, DQ_BQ), dim3(THREADS), args, 0, st);
 }
 
 }  // namespace

@@ -21,6 +21,7 @@
 // s2a_slot_pos()).
 #include "s2a_device.h"
 #include "s2a_kernels.h"
+#include "s2a_tile.h"
 
 namespace {
 
@@ -283,6 +284,223 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
   }
 }
 
+// Forward for D in {64, 128}: same math as s2a_fwd_kernel, with K/V tiles
+// in the swizzled unpadded layout of s2a_tile.h filled by direct
+// global -> LDS loads (no staging registers, addresses precomputed).
+template <int D, bool OF32>
+__global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_sw_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, void *__restrict__ o,
+    float *__restrict__ lse, S2AParams p) {
+  using T = SwTile<D>;
+  using LD = TileLoader<D, FWD_BK, FWD_THREADS / 64>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  constexpr int TILEB = FWD_BK * T::ROWB;  // bytes per tile buffer
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  char *const Ks = smem;              // two K buffers
+  char *const Vs = smem + 2 * TILEB;  // two V buffers
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, jj = bid >> 3;
+  const int lu = jj / p.tiles;
+  const int tile = p.tiles - 1 - (jj - lu * p.tiles);
+  const int u = lu * 8 + xcd;
+  if (u >= p.units) return;
+  const int gi = u % p.ngmax;
+  const int bh = u / p.ngmax;
+  const int h = bh % p.H, b = bh / p.H;
+  const int cls = h >= (p.H >> 1);
+  int base, glen;
+  if (!s2a_group(p.g, cls, gi, base, glen)) return;
+  const int q0 = tile * FWD_BQ;
+  if (q0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)b * N * rs + (size_t)h * D;
+  const bf16_t *kbh = k + boff, *vbh = v + boff;
+
+  const int qslot = q0 + 32 * w + l32;
+  const bool qin = qslot < glen;
+  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const bool qvalid = qin && qpos < L;
+
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16_t *qrow = q + boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qin) raw = *(const u32x4 *)(qrow + 16 * t + 8 * hf);
+      qreg[t] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  LD ld;
+  ld.init(w, lane);
+  auto issue = [&](int k0, int buf) {
+    char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
+    if (tile_plain(base, glen, k0, FWD_BK, N, L)) {
+      const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
+      ld.fast(kbh + r0, rs, kd);
+      ld.fast(vbh + r0, rs, vd);
+    } else {
+      ld.general(kbh, rs, base, glen, k0, N, L, kd);
+      ld.general(vbh, rs, base, glen, k0, N, L, vd);
+    }
+  };
+
+  // Per-lane byte offsets of the MFMA operand reads.
+  //   K (A of S^T): row 32*kb + l32, logical chunk 2t + hf
+  //   V^T (A of O^T, transposing read): row 16*ks + trow (+8), element
+  //   column 32*db + tcol, i.e. logical chunk 4db + 2*(grp&1) + (lane&3)/2
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+  int koff[KSTEPS], voff[DB];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) koff[t] = T::off(l32, 2 * t + hf);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    voff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
+               (lane & 1) * 8;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  constexpr float RESCALE = 8.f;
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  const int kend = min(glen, q0 + FWD_BQ);
+  const int ntiles = (kend + FWD_BK - 1) / FWD_BK;
+  const int wq_lo = q0 + 32 * w;
+  const int wq_hi = wq_lo + 31;
+  const float c2 = p.scale_log2;
+
+  issue(0, 0);
+  wait_vm_all();
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * FWD_BK;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) issue(k0 + FWD_BK, buf ^ 1);  // lands during this tile's math
+
+    if (k0 <= wq_hi) {
+      const char *Kb = Ks + buf * TILEB;
+      const char *Vb = Vs + buf * TILEB;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 a[KSTEPS];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+          a[t] = *(const bf16x8 *)(Kb + kb * 32 * T::ROWB + koff[t]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) sacc[kb] = mfma32(a[t], qreg[t], sacc[kb]);
+      }
+
+      const bool edge = (k0 + FWD_BK - 1 > wq_lo) ||
+                        !tile_plain(base, glen, k0, FWD_BK, N, L);
+      if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const bool ok =
+                ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
+            if (!ok) sacc[kb][i] = -INFINITY;
+          }
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = fmaxf(mx, wave_xor32(mx)) * c2;
+      if (__any(mx > m_ref + RESCALE)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha =
+            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e =
+              __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -m_use));
+          sacc[kb][i] = e;
+          ls += e;
+        }
+      l_run += ls;
+
+#pragma unroll
+      for (int ks = 0; ks < FWD_BK / 16; ++ks) {
+        const f32x16 &sp = sacc[ks >> 1];
+        const int e0 = 8 * (ks & 1);
+        const bf16x8 pb = to_bf16x8(sp[e0 + 0], sp[e0 + 1], sp[e0 + 2],
+                                    sp[e0 + 3], sp[e0 + 4], sp[e0 + 5],
+                                    sp[e0 + 6], sp[e0 + 7]);
+        const char *vr = Vb + 16 * ks * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x4 lo = lds_read_tr((const bf16_t *)(vr + voff[db]));
+          const bf16x4 hi =
+              lds_read_tr((const bf16_t *)(vr + 8 * T::ROWB + voff[db]));
+          oacc[db] = mfma32(cat4(lo, hi), pb, oacc[db]);
+        }
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  const float lt = l_run + wave_xor32(l_run);
+  if (qin) {
+    const float inv = qvalid ? 1.f / lt : 0.f;
+    const size_t orow = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        if (qvalid) {
+          r0 = oacc[db][4 * i4 + 0] * inv;
+          r1 = oacc[db][4 * i4 + 1] * inv;
+          r2 = oacc[db][4 * i4 + 2] * inv;
+          r3 = oacc[db][4 * i4 + 3] * inv;
+        }
+        if (OF32) {
+          f32x4 val = {r0, r1, r2, r3};
+          *(f32x4 *)((float *)o + orow + d) = val;
+        } else {
+          *(bf16x4 *)((bf16_t *)o + orow + d) = to_bf16x4(r0, r1, r2, r3);
+        }
+      }
+    if (hf == 0)
+      lse[((size_t)b * p.H + h) * N + qpos] =
+          qvalid ? (m_ref + __builtin_amdgcn_logf(lt)) * S2A_LN2 : -INFINITY;
+  }
+}
+
 template <int D, bool OF32>
 hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
                         float *lse, const S2AParams &p, hipStream_t st) {
@@ -293,8 +511,9 @@ hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
   S2AParams pp = p;
   void *args[] = {(void *)&qq, (void *)&kk, (void *)&vv, (void *)&o,
                   (void *)&lse, (void *)&pp};
-  return hipLaunchKernel((const void *)s2a_fwd_kernel<D, OF32>, grid, block,
-                         args, 0, st);
+  const void *fn = D >= 64 ? (const void *)s2a_fwd_sw_kernel<(D >= 64 ? D : 64), OF32>
+                           : (const void *)s2a_fwd_kernel<D, OF32>;
+  return hipLaunchKernel(fn, grid, block, args, 0, st);
 }
 
 }  // namespace

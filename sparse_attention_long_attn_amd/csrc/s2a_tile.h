@@ -1,0 +1,101 @@
+// Row tiles of Q/K/V/dO in LDS for head widths D in {64, 128}.
+//
+// A tile holds ROWS consecutive slots of one group as ROWS x D bf16, rows
+// back to back (no padding), filled straight from global memory with
+// global_load_lds_dwordx4: one wave instruction copies 64 chunks of 16
+// bytes, lane i landing at byte 16*i past the wave's LDS base.  Bank
+// conflicts are avoided by permuting the 16-byte chunks inside each row:
+// logical chunk c of row r sits at physical chunk c ^ swz(r).  The lane
+// that fills physical chunk p of row r therefore reads logical chunk
+// p ^ swz(r) from global memory.
+//
+// swz(r) = 2*(r mod 8) (mod chunks per row) keeps both read patterns of the
+// kernels conflict-free for D = 128:
+//   * 16-byte operand reads, 8 lanes on 8 consecutive rows, same chunk;
+//   * ds_read_b64_tr_b16, 16 lanes on 4 consecutive rows, 2 adjacent chunks
+//     each (the xor with an even value keeps a chunk pair together).
+#pragma once
+#include "s2a_device.h"
+
+template <int D>
+struct SwTile {
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;        // bytes per row
+  __device__ static constexpr int swz(int r) { return ((r & 7) << 1) & (CPR - 1); }
+  // byte offset of logical chunk c of row r
+  __device__ static constexpr int off(int r, int c) {
+    return r * ROWB + ((c ^ swz(r)) << 4);
+  }
+};
+
+// Direct global -> LDS copy of 16 bytes per lane.  lds_wave must be the
+// same for every lane of the wave (it is kept in M0).
+__device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave) {
+  __builtin_amdgcn_global_load_lds(
+      gptr, (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
+}
+
+// Loader of one ROWS-row tile of a [B,N,H,D] tensor by NWAVES waves.  Each
+// wave issues IPW instructions; instruction i of wave w fills tile chunks
+// [(w*IPW + i)*64, +64).  Per lane it keeps the tile row it fills and the
+// element offset of its logical chunk inside that row.
+template <int D, int ROWS, int NWAVES>
+struct TileLoader {
+  using T = SwTile<D>;
+  static constexpr int CHUNKS = ROWS * T::CPR;
+  static constexpr int IPW = CHUNKS / (64 * NWAVES);
+  static_assert(CHUNKS % (64 * NWAVES) == 0, "tile must split into waves");
+  int row[IPW];     // tile row filled by this lane in instruction i
+  int coff[IPW];    // element offset of its logical chunk within the row
+  int ldsb[IPW];    // wave's LDS byte offset of instruction i (uniform)
+
+  __device__ void init(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int c = (w * IPW + i) * 64 + lane;
+      const int r = c / T::CPR, pc = c % T::CPR;
+      row[i] = r;
+      coff[i] = (pc ^ T::swz(r)) * 8;
+      ldsb[i] = (w * IPW + i) * 64 * 16;
+    }
+  }
+
+  // Rows are slots s0 + row of a group; all valid and contiguous from
+  // global row pointer g0 (element pointer of slot s0's row, head h).
+  __device__ void fast(const bf16_t *g0, size_t rs, char *lds) const {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      g2lds16(g0 + (size_t)row[i] * rs + coff[i], lds + ldsb[i]);
+  }
+
+  // General rows: slot s0 + row of the group (base, glen); rows outside
+  // the group or at positions >= L read position 0 of the same (b, h)
+  // instead (finite data that the kernels mask out).
+  __device__ void general(const bf16_t *gbh, size_t rs, int base, int glen,
+                          int s0, int N, int L, char *lds) const {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = s0 + row[i];
+      int pos = 0;
+      if (s < glen) {
+        pos = s2a_slot_pos(base, s, N);
+        if (pos >= L) pos = 0;
+      }
+      g2lds16(gbh + (size_t)pos * rs + coff[i], lds + ldsb[i]);
+    }
+  }
+};
+
+// The tile [s0, s0 + rows) of a group is "plain" when every slot is inside
+// the group, the positions do not wrap and all are below L: then rows are
+// contiguous in memory from slot s0's position.
+__device__ __forceinline__ bool tile_plain(int base, int glen, int s0,
+                                           int rows, int N, int L) {
+  if (s0 + rows > glen) return false;
+  const int p0 = s2a_slot_pos(base, s0, N);
+  return p0 + rows <= L;  // L <= N, so this also rules out a wrap
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt(0);
+}
