@@ -22,6 +22,9 @@ ROOT = os.path.dirname(PKG)
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-munsafe-fp-atomics",
+    # MFMA results in VGPRs by default (long-lived accumulators are pinned
+    # to AGPRs explicitly where wanted); avoids AGPR<->VGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

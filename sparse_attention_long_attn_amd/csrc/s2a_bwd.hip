@@ -700,19 +700,20 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
 
 // dK/dV for D in {64, 128}: Q/dO tiles in the swizzled layout of
 // s2a_tile.h, filled by direct global -> LDS loads.
-template <int D>
-__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
+template <int D, int BQ>
+__global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ delta,
     float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
   using T = SwTile<D>;
-  using LD = TileLoader<D, KV_BQ, THREADS / 64>;
+  using LD = TileLoader<D, BQ, THREADS / 64>;
+  constexpr int NQB = BQ / 32;  // 32-query blocks per inner tile
   constexpr int KSTEPS = D / 16, DB = D / 32;
-  constexpr int TILEB = KV_BQ * T::ROWB;
+  constexpr int TILEB = BQ * T::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
-  __shared__ __attribute__((aligned(16))) float lse2s[2 * KV_BQ];
-  __shared__ __attribute__((aligned(16))) float dlts[2 * KV_BQ];
+  __shared__ __attribute__((aligned(16))) float lse2s[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[2 * BQ];
   char *const Qs = smem;
   char *const dOs = smem + 2 * TILEB;
 
@@ -739,7 +740,6 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   const bool kin = key < glen;
   const int kpos = kin ? s2a_slot_pos(base, key, N) : 0;
   const bool kvalid = kin && kpos < L;
-  const bool wave_keys_valid = __all(kvalid);
 
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
   {
@@ -761,7 +761,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   float l2st = INFINITY, dlst = 0.f;
   auto issue = [&](int q0, int buf) {
     char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
-    if (tile_plain(base, glen, q0, KV_BQ, N, L)) {
+    if (tile_plain(base, glen, q0, BQ, N, L)) {
       const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
       ld.fast(qbh + r0, rs, qd);
       ld.fast(gbh + r0, rs, gd);
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       ld.general(gbh, rs, base, glen, q0, N, L, gd);
     }
     // rows outside the group or padded: lse = +inf (P = 0), delta = 0
-    if (tid < KV_BQ) {
+    if (tid < BQ) {
       const int qsl = q0 + tid;
       l2st = INFINITY;
       dlst = 0.f;
@@ -784,9 +784,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     }
   };
   auto stage_stats = [&](int buf) {
-    if (tid < KV_BQ) {
-      lse2s[buf * KV_BQ + tid] = l2st;
-      dlts[buf * KV_BQ + tid] = dlst;
+    if (tid < BQ) {
+      lse2s[buf * BQ + tid] = l2st;
+      dlts[buf * BQ + tid] = dlst;
     }
   };
   int aoff[KSTEPS], troff[DB];
@@ -806,46 +806,65 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       dvacc[db][i] = 0.f;
     }
 
-  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
+  const int nq = (glen - k0 + BQ - 1) / BQ;
   issue(k0, 0);
   stage_stats(0);
   wait_vm_all();
   __syncthreads();
 
   for (int it = 0; it < nq; ++it) {
-    const int q0 = k0 + it * KV_BQ;
+    const int q0 = k0 + it * BQ;
     const int buf = it & 1;
     const bool more = it + 1 < nq;
-    if (more) issue(q0 + KV_BQ, buf ^ 1);
+    if (more) issue(q0 + BQ, buf ^ 1);
 
-    if (q0 + KV_BQ - 1 >= kw0) {
+    {
+      // Straight-line body (no skip of blocks that precede the wave's
+      // keys: the causal mask zeroes them), so the accumulators never meet
+      // a control-flow merge.
       const char *Qb = Qs + buf * TILEB;
       const char *dOb = dOs + buf * TILEB;
-      const float *l2b = lse2s + buf * KV_BQ;
-      const float *dlb = dlts + buf * KV_BQ;
-      f32x16 sacc[2], dpacc[2];
+      const float *l2b = lse2s + buf * BQ;
+      const float *dlb = dlts + buf * BQ;
+      // One block of 32 queries at a time keeps S, dP, P and dS of only
+      // that block live.  LDS reads run PIPE steps ahead of the MFMAs that
+      // consume them (an LDS read takes ~130 cycles, an MFMA 32); the
+      // scheduling fences keep the compiler from sinking them back.
+      constexpr int PIPE = 3;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        bf16x8 aq[KSTEPS], ag[KSTEPS];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          aq[t] = *(const bf16x8 *)(Qb + qb * 32 * T::ROWB + aoff[t]);
-          ag[t] = *(const bf16x8 *)(dOb + qb * 32 * T::ROWB + aoff[t]);
-        }
+      for (int qb = 0; qb < NQB; ++qb) {
+        const char *Qr = Qb + qb * 32 * T::ROWB;
+        const char *Gr = dOb + qb * 32 * T::ROWB;
+        f32x16 sacc, dpacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sacc[qb][i] = 0.f;
-          dpacc[qb][i] = 0.f;
+          sacc[i] = 0.f;
+          dpacc[i] = 0.f;
         }
+        {
+          bf16x8 aq[KSTEPS], ag[KSTEPS];
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          sacc[qb] = mfma32(aq[t], kreg[t], sacc[qb]);
-          dpacc[qb] = mfma32(ag[t], vreg[t], dpacc[qb]);
+          for (int t = 0; t < PIPE && t < KSTEPS; ++t) {
+            aq[t] = *(const bf16x8 *)(Qr + aoff[t]);
+            ag[t] = *(const bf16x8 *)(Gr + aoff[t]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < KSTEPS; ++t) {
+            if (t + PIPE < KSTEPS) {
+              aq[t + PIPE] = *(const bf16x8 *)(Qr + aoff[t + PIPE]);
+              ag[t + PIPE] = *(const bf16x8 *)(Gr + aoff[t + PIPE]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            sacc = mfma32(aq[t], kreg[t], sacc);
+            dpacc = mfma32(ag[t], vreg[t], dpacc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-      }
-      const bool edge = (q0 < kw0 + 31) || !wave_keys_valid;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        // Element i is query q0 + 32qb + 8(i/4) + 4hf + i%4.  Only blocks
+        // that reach below the wave's last key need the causal mask; keys
+        // outside the group or padded need none (their garbage stays in
+        // their own dK/dV column, written as zero at the end).
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = 32 * qb + 8 * i4 + 4 * hf;
@@ -854,33 +873,54 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c2, -l2[e]));
-            if (edge && !(kvalid && key <= q0 + r0 + e)) pp = 0.f;
-            dpacc[qb][i] = pp * (dpacc[qb][i] - dl[e]);
-            sacc[qb][i] = pp;
+            const float pp = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l2[e]));
+            dpacc[i] = pp * (dpacc[i] - dl[e]);
+            sacc[i] = pp;
           }
         }
+        if (q0 + 32 * qb < kw0 + 31) {
+          // query(i) - key = d0 + 8(i/4) + i%4; masked where negative
+          const int d0 = q0 + 32 * qb + 4 * hf - key;
 #pragma unroll
-      for (int qs = 0; qs < KV_BQ / 16; ++qs) {
-        const int e0 = 8 * (qs & 1);
-        const f32x16 &sp = sacc[qs >> 1];
-        const f32x16 &dp = dpacc[qs >> 1];
-        const bf16x8 pb = to_bf16x8(sp[e0], sp[e0 + 1], sp[e0 + 2], sp[e0 + 3],
-                                    sp[e0 + 4], sp[e0 + 5], sp[e0 + 6], sp[e0 + 7]);
-        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
-                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
-        const char *gr = dOb + 16 * qs * T::ROWB;
-        const char *qr = Qb + 16 * qs * T::ROWB;
+          for (int i = 0; i < 16; ++i)
+            if (d0 + 8 * (i >> 2) + (i & 3) < 0) {
+              sacc[i] = 0.f;
+              dpacc[i] = 0.f;
+            }
+        }
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ag = cat4(
-              lds_read_tr((const bf16_t *)(gr + troff[db])),
-              lds_read_tr((const bf16_t *)(gr + 8 * T::ROWB + troff[db])));
-          dvacc[db] = mfma32(ag, pb, dvacc[db]);
-          const bf16x8 aq = cat4(
-              lds_read_tr((const bf16_t *)(qr + troff[db])),
-              lds_read_tr((const bf16_t *)(qr + 8 * T::ROWB + troff[db])));
-          dkacc[db] = mfma32(aq, sb, dkacc[db]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int e0 = 8 * h2;
+          pb[h2] = to_bf16x8(sacc[e0], sacc[e0 + 1], sacc[e0 + 2], sacc[e0 + 3],
+                             sacc[e0 + 4], sacc[e0 + 5], sacc[e0 + 6], sacc[e0 + 7]);
+          sb[h2] = to_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3],
+                             dpacc[e0 + 4], dpacc[e0 + 5], dpacc[e0 + 6], dpacc[e0 + 7]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries:
+        // step st = (h2, db) of 2 MFMAs, operands from transposing reads.
+        constexpr int NST = 2 * DB;
+        bf16x8 tg[NST], tq[NST];
+        auto tload = [&](int st) {
+          const int h2 = st / DB, db = st % DB;
+          const char *gr = Gr + 16 * h2 * T::ROWB + troff[db];
+          const char *qr = Qr + 16 * h2 * T::ROWB + troff[db];
+          tg[st] = cat4(lds_read_tr((const bf16_t *)gr),
+                        lds_read_tr((const bf16_t *)(gr + 8 * T::ROWB)));
+          tq[st] = cat4(lds_read_tr((const bf16_t *)qr),
+                        lds_read_tr((const bf16_t *)(qr + 8 * T::ROWB)));
+        };
+#pragma unroll
+        for (int st = 0; st < PIPE && st < NST; ++st) tload(st);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          if (st + PIPE < NST) tload(st + PIPE);
+          __builtin_amdgcn_sched_barrier(0);
+          const int h2 = st / DB, db = st % DB;
+          mfma32_agpr(dvacc[db], tg[st], pb[h2]);
+          mfma32_agpr(dkacc[db], tq[st], sb[h2]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -889,17 +929,23 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     __syncthreads();
   }
 
+  mfma_agpr_drain();
   if (kin) {
     const size_t row = boff + (size_t)kpos * rs;
+    const float ks = kvalid ? p.scale : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = 32 * db + 8 * i4 + 4 * hf;
-        const f32x4 kk = {dkacc[db][4 * i4] * p.scale, dkacc[db][4 * i4 + 1] * p.scale,
-                          dkacc[db][4 * i4 + 2] * p.scale, dkacc[db][4 * i4 + 3] * p.scale};
-        const f32x4 vv = {dvacc[db][4 * i4], dvacc[db][4 * i4 + 1],
-                          dvacc[db][4 * i4 + 2], dvacc[db][4 * i4 + 3]};
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+        if (kvalid) {  // a padded key's column holds garbage, not gradient
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kk[e] = dkacc[db][4 * i4 + e] * ks;
+            vv[e] = dvacc[db][4 * i4 + e];
+          }
+        }
         *(f32x4 *)(dk + row + d) = kk;
         *(f32x4 *)(dv + row + d) = vv;
       }
@@ -937,7 +983,7 @@ hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
                   (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
                   (void *)&p};
   const void *fn = D >= 64
-                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64)>
+                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64), KV_BQ>
                        : (const void *)s2a_bwd_dkdv_kernel<D>;
   return hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
 }

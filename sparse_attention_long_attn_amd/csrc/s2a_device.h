@@ -37,6 +37,25 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Accumulate-only form of mfma32 whose accumulator stays in AGPRs (the
+// compiler otherwise shuffles long-lived accumulators between register
+// files under pressure).  The leading s_nop covers the wait states a VALU
+// write of a or b needs before an MFMA reads it.  Back-to-back chaining on
+// the same accumulator needs none; before the accumulator is read by
+// anything but this form, call mfma_agpr_drain().
+__device__ __forceinline__ void mfma32_agpr(f32x16 &acc, const bf16x8 &a,
+                                            const bf16x8 &b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+      : "+a"(acc)
+      : "v"(a), "v"(b));
+}
+
+// Wait states between the last mfma32_agpr and a read of its accumulator
+// (a 16-pass MFMA needs 18).
+__device__ __forceinline__ void mfma_agpr_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // LDS transposing read: within each group of 16 lanes, lanes 4r..4r+3 each
 // name 4 consecutive 16-bit elements that together form row r (r = 0..3);
 // lane i of the group receives column i of those four rows.
