@@ -23,6 +23,8 @@
 // recomputed) but replaces fp32 atomics whose traffic (one read-modify-
 // write of a 64x128 fp32 tile per key tile and query tile) cost more than
 // the whole rest of the backward.
+#include <type_traits>
+
 #include "s2a_device.h"
 #include "s2a_kernels.h"
 #include "s2a_tile.h"
@@ -33,7 +35,9 @@ constexpr int KV_BK = 128;   // keys per dK/dV workgroup, 32 per wave
 constexpr int KV_BQ = 64;    // queries per inner tile of the dK/dV kernel
 constexpr int DQ_BQ = 128;   // queries per dQ workgroup, 32 per wave
 constexpr int DQ_BK = 64;    // keys per inner tile of the dQ kernel
-constexpr int THREADS = 256;
+constexpr int THREADS = 256;      // dK/dV workgroup
+constexpr int DQ_THREADS = DQ_BQ / 32 * 64;
+constexpr int DQ_MINBLOCKS = 512 / DQ_THREADS;  // two waves per SIMD
 
 template <int D>
 struct BwdDims {
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
 // dQ (query-outer)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
+__global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ delta,
@@ -351,8 +355,8 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
   using Dm = BwdDims<D>;
   constexpr int KP = Dm::KP;
   constexpr int TILE = DQ_BK * KP;
-  constexpr int NCH = DQ_BK * Dm::CPR / THREADS;
-  static_assert(DQ_BK * Dm::CPR % THREADS == 0, "tile split");
+  constexpr int TCH = DQ_BK * Dm::CPR;                  // chunks per tile
+  constexpr int NCH = (TCH + DQ_THREADS - 1) / DQ_THREADS;    // chunks per thread
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
 
@@ -400,11 +404,11 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * THREADS;
+      const int c = tid + i * DQ_THREADS;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       const int ks = k0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (ks < glen && ch * 8 < D) {
+      if (c < TCH && ks < glen && ch * 8 < D) {
         const int kp = s2a_slot_pos(base, ks, N);
         if (kp < L) {
           const size_t off = boff + (size_t)kp * rs + ch * 8;
@@ -419,7 +423,8 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * THREADS;
+      const int c = tid + i * DQ_THREADS;
+      if (c >= TCH) continue;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       *(u32x4 *)(Ks + buf * TILE + r * KP + ch * 8) = kst[i];
       *(u32x4 *)(Vs + buf * TILE + r * KP + ch * 8) = vst[i];
@@ -527,13 +532,13 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_kernel(
 // dQ for D in {64, 128}: K/V tiles in the swizzled layout of s2a_tile.h,
 // filled by direct global -> LDS loads.
 template <int D>
-__global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
+__global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ delta,
     float *__restrict__ dq, S2AParams p) {
   using T = SwTile<D>;
-  using LD = TileLoader<D, DQ_BK, THREADS / 64>;
+  using LD = TileLoader<D, DQ_BK, DQ_THREADS / 64>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = DQ_BK * T::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
@@ -593,13 +598,16 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
       ld.general(vbh, rs, base, glen, k0, N, L, vd);
     }
   };
-  int aoff[KSTEPS], troff[DB];
+  // (rows trow and trow + 8 of a 16-row step have different swizzles)
+  int aoff[KSTEPS], troff[DB], troff8[DB];
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) aoff[t] = T::off(l32, 2 * t + hf);
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    troff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
-                (lane & 1) * 8;
+  for (int db = 0; db < DB; ++db) {
+    const int c = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
+    troff[db] = T::off(trow, c) + (lane & 1) * 8;
+    troff8[db] = T::off(trow + 8, c) + (lane & 1) * 8;
+  }
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -668,9 +676,8 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
         const char *kr = Kb + 16 * ks * T::ROWB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 ak = cat4(
-              lds_read_tr((const bf16_t *)(kr + troff[db])),
-              lds_read_tr((const bf16_t *)(kr + 8 * T::ROWB + troff[db])));
+          const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[db])),
+                                 lds_read_tr((const bf16_t *)(kr + troff8[db])));
           dqacc[db] = mfma32(ak, sb, dqacc[db]);
         }
       }
@@ -699,23 +706,27 @@ __global__ __launch_bounds__(THREADS, 2) void s2a_bwd_dq_sw_kernel(
 }
 
 // dK/dV for D in {64, 128}: Q/dO tiles in the swizzled layout of
-// s2a_tile.h, filled by direct global -> LDS loads.
-template <int D, int BQ>
-__global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_kernel(
+// s2a_tile.h, filled by direct global -> LDS loads NBUF-1 tiles ahead.
+// The first iterations (the only ones whose queries can precede the
+// workgroup's keys) run a masked copy of the body; the steady state has no
+// mask at all.
+template <int D, int BQ, int NBUF>
+__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ delta,
     float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
   using T = SwTile<D>;
   using LD = TileLoader<D, BQ, THREADS / 64>;
-  constexpr int NQB = BQ / 32;  // 32-query blocks per inner tile
+  constexpr int NQB = BQ / 32;  // 32-query blocks per tile
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = BQ * T::ROWB;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
-  __shared__ __attribute__((aligned(16))) float lse2s[2 * BQ];
-  __shared__ __attribute__((aligned(16))) float dlts[2 * BQ];
+  constexpr int NG2L = 2 * LD::IPW;  // direct loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * TILEB];
+  __shared__ __attribute__((aligned(16))) float lse2s[NBUF * BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[NBUF * BQ];
   char *const Qs = smem;
-  char *const dOs = smem + 2 * TILEB;
+  char *const dOs = smem + NBUF * TILEB;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -758,18 +769,10 @@ __global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_k
 
   LD ld;
   ld.init(w, lane);
+  // Per-row statistics of a query tile, through registers: rows outside
+  // the group or padded get lse = +inf (so P = 0) and delta = 0.
   float l2st = INFINITY, dlst = 0.f;
-  auto issue = [&](int q0, int buf) {
-    char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
-    if (tile_plain(base, glen, q0, BQ, N, L)) {
-      const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
-      ld.fast(qbh + r0, rs, qd);
-      ld.fast(gbh + r0, rs, gd);
-    } else {
-      ld.general(qbh, rs, base, glen, q0, N, L, qd);
-      ld.general(gbh, rs, base, glen, q0, N, L, gd);
-    }
-    // rows outside the group or padded: lse = +inf (P = 0), delta = 0
+  auto fetch_stats = [&](int q0) {
     if (tid < BQ) {
       const int qsl = q0 + tid;
       l2st = INFINITY;
@@ -789,13 +792,27 @@ __global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_k
       dlts[buf * BQ + tid] = dlst;
     }
   };
-  int aoff[KSTEPS], troff[DB];
+  auto issue_tile = [&](int q0, int buf) {
+    char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
+    if (tile_plain(base, glen, q0, BQ, N, L)) {
+      const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
+      ld.fast(qbh + r0, rs, qd);
+      ld.fast(gbh + r0, rs, gd);
+    } else {
+      ld.general(qbh, rs, base, glen, q0, N, L, qd);
+      ld.general(gbh, rs, base, glen, q0, N, L, gd);
+    }
+  };
+  // (rows trow and trow + 8 of a 16-row step have different swizzles)
+  int aoff[KSTEPS], troff[DB], troff8[DB];
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) aoff[t] = T::off(l32, 2 * t + hf);
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    troff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
-                (lane & 1) * 8;
+  for (int db = 0; db < DB; ++db) {
+    const int c = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
+    troff[db] = T::off(trow, c) + (lane & 1) * 8;
+    troff8[db] = T::off(trow + 8, c) + (lane & 1) * 8;
+  }
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -807,132 +824,175 @@ __global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_k
     }
 
   const int nq = (glen - k0 + BQ - 1) / BQ;
-  issue(k0, 0);
-  stage_stats(0);
+#pragma unroll
+  for (int s0 = 0; s0 < NBUF - 1; ++s0)
+    if (s0 < nq) {
+      fetch_stats(k0 + s0 * BQ);
+      wait_vm_all();
+      stage_stats(s0);
+      issue_tile(k0 + s0 * BQ, s0);
+    }
   wait_vm_all();
   __syncthreads();
 
-  for (int it = 0; it < nq; ++it) {
+  auto body = [&](auto masked_tag, int it) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int q0 = k0 + it * BQ;
-    const int buf = it & 1;
-    const bool more = it + 1 < nq;
-    if (more) issue(q0 + BQ, buf ^ 1);
-
-    {
-      // Straight-line body (no skip of blocks that precede the wave's
-      // keys: the causal mask zeroes them), so the accumulators never meet
-      // a control-flow merge.
-      const char *Qb = Qs + buf * TILEB;
-      const char *dOb = dOs + buf * TILEB;
-      const float *l2b = lse2s + buf * BQ;
-      const float *dlb = dlts + buf * BQ;
-      // One block of 32 queries at a time keeps S, dP, P and dS of only
-      // that block live.  LDS reads run PIPE steps ahead of the MFMAs that
-      // consume them (an LDS read takes ~130 cycles, an MFMA 32); the
-      // scheduling fences keep the compiler from sinking them back.
-      constexpr int PIPE = 3;
+    const int buf = it % NBUF;
+    const int pre = it + NBUF - 1;  // tile loaded during this iteration
+    if (pre < nq) {
+      fetch_stats(k0 + pre * BQ);   // issued before the tile: waited first
+      issue_tile(k0 + pre * BQ, pre % NBUF);
+    }
+    const char *Qb = Qs + buf * TILEB;
+    const char *dOb = dOs + buf * TILEB;
+    const float *l2b = lse2s + buf * BQ;
+    const float *dlb = dlts + buf * BQ;
+    static_assert(NQB == 2, "the pipeline below is written for two blocks");
+    // Software pipeline over the tile's two 32-query blocks, one wave per
+    // SIMD, so the matrix unit and the VALU work on different blocks:
+    //   P1  S, dP of block 0                      (MFMA)
+    //   P2  S, dP of block 1      || P, dS of block 0     (MFMA || VALU)
+    //   P3  dV, dK of block 0     || P, dS of block 1
+    //   P4  dV, dK of block 1
+    // Each step issues LDS reads PIPE steps ahead, then its two MFMAs and a
+    // slice of the other block's element work; the scheduling fences pin
+    // that order.  Element i of a block is query 8(i/4) + 4hf + i%4 of the
+    // block; keys outside the group need no mask (their garbage stays in
+    // their own dK/dV column, written as zero at the end).
+    constexpr int PIPE = 3;
+    f32x4 l2v[2][4], dlv[2][4];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const char *Qr = Qb + qb * 32 * T::ROWB;
-        const char *Gr = dOb + qb * 32 * T::ROWB;
-        f32x16 sacc, dpacc;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = 0.f;
-          dpacc[i] = 0.f;
-        }
-        {
-          bf16x8 aq[KSTEPS], ag[KSTEPS];
-#pragma unroll
-          for (int t = 0; t < PIPE && t < KSTEPS; ++t) {
-            aq[t] = *(const bf16x8 *)(Qr + aoff[t]);
-            ag[t] = *(const bf16x8 *)(Gr + aoff[t]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int t = 0; t < KSTEPS; ++t) {
-            if (t + PIPE < KSTEPS) {
-              aq[t + PIPE] = *(const bf16x8 *)(Qr + aoff[t + PIPE]);
-              ag[t + PIPE] = *(const bf16x8 *)(Gr + aoff[t + PIPE]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            sacc = mfma32(aq[t], kreg[t], sacc);
-            dpacc = mfma32(ag[t], vreg[t], dpacc);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        // Element i is query q0 + 32qb + 8(i/4) + 4hf + i%4.  Only blocks
-        // that reach below the wave's last key need the causal mask; keys
-        // outside the group or padded need none (their garbage stays in
-        // their own dK/dV column, written as zero at the end).
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = 32 * qb + 8 * i4 + 4 * hf;
-          const f32x4 l2 = *(const f32x4 *)(l2b + r0);
-          const f32x4 dl = *(const f32x4 *)(dlb + r0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const float pp = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l2[e]));
-            dpacc[i] = pp * (dpacc[i] - dl[e]);
-            sacc[i] = pp;
-          }
-        }
-        if (q0 + 32 * qb < kw0 + 31) {
-          // query(i) - key = d0 + 8(i/4) + i%4; masked where negative
-          const int d0 = q0 + 32 * qb + 4 * hf - key;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (d0 + 8 * (i >> 2) + (i & 3) < 0) {
-              sacc[i] = 0.f;
-              dpacc[i] = 0.f;
-            }
-        }
-        bf16x8 pb[2], sb[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int e0 = 8 * h2;
-          pb[h2] = to_bf16x8(sacc[e0], sacc[e0 + 1], sacc[e0 + 2], sacc[e0 + 3],
-                             sacc[e0 + 4], sacc[e0 + 5], sacc[e0 + 6], sacc[e0 + 7]);
-          sb[h2] = to_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2], dpacc[e0 + 3],
-                             dpacc[e0 + 4], dpacc[e0 + 5], dpacc[e0 + 6], dpacc[e0 + 7]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries:
-        // step st = (h2, db) of 2 MFMAs, operands from transposing reads.
-        constexpr int NST = 2 * DB;
-        bf16x8 tg[NST], tq[NST];
-        auto tload = [&](int st) {
-          const int h2 = st / DB, db = st % DB;
-          const char *gr = Gr + 16 * h2 * T::ROWB + troff[db];
-          const char *qr = Qr + 16 * h2 * T::ROWB + troff[db];
-          tg[st] = cat4(lds_read_tr((const bf16_t *)gr),
-                        lds_read_tr((const bf16_t *)(gr + 8 * T::ROWB)));
-          tq[st] = cat4(lds_read_tr((const bf16_t *)qr),
-                        lds_read_tr((const bf16_t *)(qr + 8 * T::ROWB)));
-        };
-#pragma unroll
-        for (int st = 0; st < PIPE && st < NST; ++st) tload(st);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          if (st + PIPE < NST) tload(st + PIPE);
-          __builtin_amdgcn_sched_barrier(0);
-          const int h2 = st / DB, db = st % DB;
-          mfma32_agpr(dvacc[db], tg[st], pb[h2]);
-          mfma32_agpr(dkacc[db], tq[st], sb[h2]);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        l2v[qb][i4] = *(const f32x4 *)(l2b + 32 * qb + 8 * i4 + 4 * hf);
+        dlv[qb][i4] = *(const f32x4 *)(dlb + 32 * qb + 8 * i4 + 4 * hf);
+      }
+    f32x16 S[2], dP[2];
+    bf16x8 pb[2][2], sb[2][2];
+    // element work of block qb: P = exp2(S c - lse2), dS = P (dP - delta)
+    auto elem = [&](int qb, int i) {
+      float pp = __builtin_amdgcn_exp2f(fmaf(S[qb][i], c2, -l2v[qb][i >> 2][i & 3]));
+      float ds = pp * (dP[qb][i] - dlv[qb][i >> 2][i & 3]);
+      if (MASKED) {
+        const int d0 = q0 + 32 * qb + 4 * hf - key;  // query - key
+        if (d0 + 8 * (i >> 2) + (i & 3) < 0) {
+          pp = 0.f;
+          ds = 0.f;
         }
       }
+      S[qb][i] = pp;
+      dP[qb][i] = ds;
+    };
+    auto pack = [&](int qb, int h2) {
+      const int e0 = 8 * h2;
+      pb[qb][h2] = to_bf16x8(S[qb][e0], S[qb][e0 + 1], S[qb][e0 + 2], S[qb][e0 + 3],
+                             S[qb][e0 + 4], S[qb][e0 + 5], S[qb][e0 + 6], S[qb][e0 + 7]);
+      sb[qb][h2] = to_bf16x8(dP[qb][e0], dP[qb][e0 + 1], dP[qb][e0 + 2], dP[qb][e0 + 3],
+                             dP[qb][e0 + 4], dP[qb][e0 + 5], dP[qb][e0 + 6], dP[qb][e0 + 7]);
+    };
+    // S, dP operands (16-byte reads) of block qb, step t
+    bf16x8 aq[2][KSTEPS], ag[2][KSTEPS];
+    auto spload = [&](int qb, int t) {
+      aq[qb][t] = *(const bf16x8 *)(Qb + qb * 32 * T::ROWB + aoff[t]);
+      ag[qb][t] = *(const bf16x8 *)(dOb + qb * 32 * T::ROWB + aoff[t]);
+    };
+    // dV, dK operands (transposing reads) of block qb, step st = (h2, db)
+    constexpr int NST = 2 * DB;
+    bf16x8 tg[2][NST], tq[2][NST];
+    auto dkload = [&](int qb, int st) {
+      const int h2 = st / DB, db = st % DB;
+      const char *gr = dOb + (qb * 32 + 16 * h2) * T::ROWB;
+      const char *qr = Qb + (qb * 32 + 16 * h2) * T::ROWB;
+      tg[qb][st] = cat4(lds_read_tr((const bf16_t *)(gr + troff[db])),
+                        lds_read_tr((const bf16_t *)(gr + troff8[db])));
+      tq[qb][st] = cat4(lds_read_tr((const bf16_t *)(qr + troff[db])),
+                        lds_read_tr((const bf16_t *)(qr + troff8[db])));
+    };
+    auto spmfma = [&](int qb, int t) {
+      S[qb] = mfma32(aq[qb][t], kreg[t], S[qb]);
+      dP[qb] = mfma32(ag[qb][t], vreg[t], dP[qb]);
+    };
+    auto dkmfma = [&](int qb, int st) {
+      const int h2 = st / DB, db = st % DB;
+      mfma32_agpr(dvacc[db], tg[qb][st], pb[qb][h2]);
+      mfma32_agpr(dkacc[db], tq[qb][st], sb[qb][h2]);
+    };
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        S[qb][i] = 0.f;
+        dP[qb][i] = 0.f;
+      }
+
+    // P1
+#pragma unroll
+    for (int t = 0; t < PIPE; ++t) spload(0, t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      if (t + PIPE < KSTEPS) spload(0, t + PIPE);
+      else spload(1, t + PIPE - KSTEPS);
+      __builtin_amdgcn_sched_barrier(0);
+      spmfma(0, t);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) stage_stats(buf ^ 1);
-    wait_vm_all();
+    // P2
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      if (t + PIPE < KSTEPS) spload(1, t + PIPE);
+      else dkload(0, t + PIPE - KSTEPS);
+      __builtin_amdgcn_sched_barrier(0);
+      spmfma(1, t);
+      constexpr int EPS = 16 / KSTEPS;  // elements per step
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) elem(0, EPS * t + e);
+      if (EPS * (t + 1) == 8) pack(0, 0);
+      if (t == KSTEPS - 1) pack(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P3
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + PIPE < NST) dkload(0, st + PIPE);
+      else dkload(1, st + PIPE - NST);
+      __builtin_amdgcn_sched_barrier(0);
+      dkmfma(0, st);
+      constexpr int EPS = 16 / NST;  // elements per step
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) elem(1, EPS * st + e);
+      if (EPS * (st + 1) == 8) pack(1, 0);
+      if (st == NST - 1) pack(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P4
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + PIPE < NST) dkload(1, st + PIPE);
+      __builtin_amdgcn_sched_barrier(0);
+      dkmfma(1, st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (pre < nq) {
+      wait_vm<NG2L>();  // all but this iteration's tile loads have landed
+      stage_stats(pre % NBUF);
+    } else {
+      wait_vm_all();
+    }
     __syncthreads();
-  }
+  };
+
+  // Iterations whose queries can precede some of the workgroup's keys.
+  const int npeel = min(nq, (KV_BK + BQ - 1) / BQ);
+  int it = 0;
+  for (; it < npeel; ++it) body(std::true_type{}, it);
+  for (; it < nq; ++it) body(std::false_type{}, it);
 
   mfma_agpr_drain();
   if (kin) {
     const size_t row = boff + (size_t)kpos * rs;
-    const float ks = kvalid ? p.scale : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -942,7 +1002,7 @@ __global__ __launch_bounds__(THREADS, (BQ <= 32 ? 2 : 1)) void s2a_bwd_dkdv_sw_k
         if (kvalid) {  // a padded key's column holds garbage, not gradient
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            kk[e] = dkacc[db][4 * i4 + e] * ks;
+            kk[e] = dkacc[db][4 * i4 + e] * p.scale;
             vv[e] = dvacc[db][4 * i4 + e];
           }
         }
@@ -983,7 +1043,7 @@ hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
                   (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
                   (void *)&p};
   const void *fn = D >= 64
-                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64), KV_BQ>
+                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64), KV_BQ, 2>
                        : (const void *)s2a_bwd_dkdv_kernel<D>;
   return hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
 }
@@ -1000,7 +1060,7 @@ hipError_t launch_dq_t(const void *q, const void *k, const void *v,
   const void *fn = D >= 64
                        ? (const void *)s2a_bwd_dq_sw_kernel<(D >= 64 ? D : 64)>
                        : (const void *)s2a_bwd_dq_kernel<D>;
-  return hipLaunchKernel(fn, unit_grid(p, DQ_BQ), dim3(THREADS), args, 0, st);
+  return hipLaunchKernel(fn, unit_grid(p, DQ_BQ), dim3(DQ_THREADS), args, 0, st);
 }
 
 }  // namespace

@@ -27,7 +27,9 @@ namespace {
 
 constexpr int FWD_BQ = 128;  // query rows per workgroup, 32 per wave
 constexpr int FWD_BK = 64;   // keys per LDS tile
-constexpr int FWD_THREADS = 256;
+constexpr int FWD_THREADS = FWD_BQ / 32 * 64;
+// two waves per SIMD: 256-thread groups two per CU, 512-thread groups one
+constexpr int FWD_MINBLOCKS = 512 / FWD_THREADS;
 
 template <int D>
 struct FwdDims {
@@ -48,15 +50,15 @@ __device__ __forceinline__ bool tile_has_padding(int base, int k0, int kend,
 }
 
 template <int D, bool OF32>
-__global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
+__global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
     float *__restrict__ lse, S2AParams p) {
   using Dm = FwdDims<D>;
   constexpr int KP = Dm::KP;
   constexpr int TILE = FWD_BK * KP;                       // elements per buffer
-  constexpr int NCH = FWD_BK * Dm::CPR / FWD_THREADS;     // chunks per thread
-  static_assert(FWD_BK * Dm::CPR % FWD_THREADS == 0, "tile split");
+  constexpr int TCH = FWD_BK * Dm::CPR;                  // chunks per tile
+  constexpr int NCH = (TCH + FWD_THREADS - 1) / FWD_THREADS;    // chunks per thread
   // Two K and two V buffers: tile t+1 is written while tile t is read.
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       const int ks = k0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (ks < glen && ch * 8 < D) {
+      if (c < TCH && ks < glen && ch * 8 < D) {
         const int kp = s2a_slot_pos(base, ks, N);
         if (kp < L) {
           const size_t off = boff + (size_t)kp * rs + ch * 8;
@@ -129,6 +131,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * FWD_THREADS;
+      if (c >= TCH) continue;
       const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
       *(u32x4 *)(Ks + buf * TILE + r * KP + ch * 8) = kst[i];
       *(u32x4 *)(Vs + buf * TILE + r * KP + ch * 8) = vst[i];
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_kernel(
 // in the swizzled unpadded layout of s2a_tile.h filled by direct
 // global -> LDS loads (no staging registers, addresses precomputed).
 template <int D, bool OF32>
-__global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_sw_kernel(
+__global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
     float *__restrict__ lse, S2AParams p) {
@@ -359,13 +362,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_sw_kernel(
   //   column 32*db + tcol, i.e. logical chunk 4db + 2*(grp&1) + (lane&3)/2
   const int grp = lane >> 4;
   const int trow = 4 * hf + ((lane & 15) >> 2);
-  int koff[KSTEPS], voff[DB];
+  // (rows trow and trow + 8 of a 16-key step have different swizzles)
+  int koff[KSTEPS], voff[DB], voff8[DB];
 #pragma unroll
   for (int t = 0; t < KSTEPS; ++t) koff[t] = T::off(l32, 2 * t + hf);
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    voff[db] = T::off(trow, 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1)) +
-               (lane & 1) * 8;
+  for (int db = 0; db < DB; ++db) {
+    const int c = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
+    voff[db] = T::off(trow, c) + (lane & 1) * 8;
+    voff8[db] = T::off(trow + 8, c) + (lane & 1) * 8;
+  }
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -462,8 +468,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void s2a_fwd_sw_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x4 lo = lds_read_tr((const bf16_t *)(vr + voff[db]));
-          const bf16x4 hi =
-              lds_read_tr((const bf16_t *)(vr + 8 * T::ROWB + voff[db]));
+          const bf16x4 hi = lds_read_tr((const bf16_t *)(vr + voff8[db]));
           oacc[db] = mfma32(cat4(lo, hi), pb, oacc[db]);
         }
       }
