@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device-to-device (a plain copy "
+                         "kernel of known size, to calibrate HBM counters)")
     return ap.parse_args()
 
 
@@ -148,6 +151,15 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)            # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -179,9 +191,9 @@ def main():
     # in the dQ kernel, which also recomputes S and dP (not counted)
     D_pairs = f_fwd // (4 * D)
     kernels = {
-        "s2a_fwd_kernel": (fwd_ms, f_fwd),
-        "s2a_bwd_dkdv_kernel": (dkdv_ms, 8 * D * D_pairs),
-        "s2a_bwd_dq_kernel": (dq_ms, 2 * D * D_pairs),
+        "s2a_fwd_sw_kernel": (fwd_ms, f_fwd),
+        "s2a_bwd_dkdv_sw_kernel": (dkdv_ms, 8 * D * D_pairs),
+        "s2a_bwd_dq_sw_kernel": (dq_ms, 2 * D * D_pairs),
     }
     dom = max(kernels, key=lambda n: kernels[n][0])
     dms, dfl = kernels[dom]
