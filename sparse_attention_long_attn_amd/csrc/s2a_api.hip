@@ -41,10 +41,13 @@ s2a_status check_shape(int B, int N, int H, int D, int G, int shift,
     return fail(S2A_EINVAL, "boundary=%lld is neither WRAP nor SPLIT", boundary);
   if (D != 16 && D != 32 && D != 64 && D != 128)
     return fail(S2A_EUNSUPPORTED, "head width D=%lld not in {16,32,64,128}", D);
-  // Offsets of a row are formed in 64 bits; positions and grid sizes in 32.
+  // Offsets of a row are formed in 64 bits; positions and grid sizes in 32;
+  // offsets inside one 128-row tile in 32 (128 * H * D * 2 bytes < 2^32).
   const long long units = (long long)B * H * (N / G + 1);
   if ((long long)B * N > (1ll << 31) || units * (G / 16 + 1) > (1ll << 31))
     return fail(S2A_EINVAL, "problem too large for one launch");
+  if ((long long)H * D >= (1ll << 24))
+    return fail(S2A_EUNSUPPORTED, "H*D=%lld is 2^24 or more", (long long)H * D);
   return S2A_OK;
 }
 
@@ -119,7 +122,7 @@ s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, s2a_fwd_tile_rows());
+                                  scale, s2a_fwd_tile_rows(D));
   return hip_status(s2a_launch_fwd(q, k, v, o, o_dtype == S2A_F32, lse, D, p,
                                    (hipStream_t)stream),
                     "forward launch");

@@ -587,12 +587,13 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 
   LD ld;
   ld.init(w, lane);
+  ld.init_rs(rs);
   auto issue = [&](int k0, int buf) {
     char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
     if (tile_plain(base, glen, k0, DQ_BK, N, L)) {
       const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
-      ld.fast(kbh + r0, rs, kd);
-      ld.fast(vbh + r0, rs, vd);
+      ld.fast_s(kbh + r0, kd);
+      ld.fast_s(vbh + r0, vd);
     } else {
       ld.general(kbh, rs, base, glen, k0, N, L, kd);
       ld.general(vbh, rs, base, glen, k0, N, L, vd);
@@ -769,6 +770,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 
   LD ld;
   ld.init(w, lane);
+  ld.init_rs(rs);
   // Per-row statistics of a query tile, through registers: rows outside
   // the group or padded get lse = +inf (so P = 0) and delta = 0.
   float l2st = INFINITY, dlst = 0.f;
@@ -796,8 +798,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
     if (tile_plain(base, glen, q0, BQ, N, L)) {
       const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
-      ld.fast(qbh + r0, rs, qd);
-      ld.fast(gbh + r0, rs, gd);
+      ld.fast_s(qbh + r0, qd);
+      ld.fast_s(gbh + r0, gd);
     } else {
       ld.general(qbh, rs, base, glen, q0, N, L, qd);
       ld.general(gbh, rs, base, glen, q0, N, L, gd);

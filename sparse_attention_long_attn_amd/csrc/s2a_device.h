@@ -82,6 +82,18 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2,
   return __builtin_convertvector(f, bf16x4);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// max / sum of x over lanes l and l^32, with v_permlane32_swap (a VALU
+// cross-half swap: both registers start as x; afterwards lane l holds x of
+// lanes l and l^32 between them).  Written as asm because the builtin's
+// second result is not returned correctly by this compiler.
+__device__ __forceinline__ float wave_max_x32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
 }
+__device__ __forceinline__ float wave_sum_x32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, wave_xor32(mx)) * c2;
+      mx = wave_max_x32(mx) * c2;
       if (__any(mx > m_ref + RESCALE)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha =
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   }
 
   // Epilogue: normalise, write O and LSE at the original position.
-  const float lt = l_run + wave_xor32(l_run);
+  const float lt = wave_sum_x32(l_run);
   if (qin) {
     const float inv = qvalid ? 1.f / lt : 0.f;
     const size_t orow = boff + (size_t)qpos * rs;
@@ -344,12 +344,13 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
 
   LD ld;
   ld.init(w, lane);
+  ld.init_rs(rs);
   auto issue = [&](int k0, int buf) {
     char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
     if (tile_plain(base, glen, k0, FWD_BK, N, L)) {
       const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
-      ld.fast(kbh + r0, rs, kd);
-      ld.fast(vbh + r0, rs, vd);
+      ld.fast_s(kbh + r0, kd);
+      ld.fast_s(vbh + r0, vd);
     } else {
       ld.general(kbh, rs, base, glen, k0, N, L, kd);
       ld.general(vbh, rs, base, glen, k0, N, L, vd);
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, wave_xor32(mx)) * c2;
+      mx = wave_max_x32(mx) * c2;
       if (__any(mx > m_ref + RESCALE)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha =
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     __syncthreads();
   }
 
-  const float lt = l_run + wave_xor32(l_run);
+  const float lt = wave_sum_x32(l_run);
   if (qin) {
     const float inv = qvalid ? 1.f / lt : 0.f;
     const size_t orow = boff + (size_t)qpos * rs;
@@ -510,20 +511,20 @@ template <int D, bool OF32>
 hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
                         float *lse, const S2AParams &p, hipStream_t st) {
   const int units_pad = (p.units + 7) / 8 * 8;
-  dim3 grid((unsigned)units_pad * (unsigned)p.tiles), block(FWD_THREADS);
   const bf16_t *qq = (const bf16_t *)q, *kk = (const bf16_t *)k,
                *vv = (const bf16_t *)v;
   S2AParams pp = p;
   void *args[] = {(void *)&qq, (void *)&kk, (void *)&vv, (void *)&o,
                   (void *)&lse, (void *)&pp};
+  dim3 grid((unsigned)units_pad * (unsigned)p.tiles);
   const void *fn = D >= 64 ? (const void *)s2a_fwd_sw_kernel<(D >= 64 ? D : 64), OF32>
                            : (const void *)s2a_fwd_kernel<D, OF32>;
-  return hipLaunchKernel(fn, grid, block, args, 0, st);
+  return hipLaunchKernel(fn, grid, dim3(FWD_THREADS), args, 0, st);
 }
 
 }  // namespace
 
-int s2a_fwd_tile_rows() { return FWD_BQ; }
+int s2a_fwd_tile_rows(int) { return FWD_BQ; }
 
 hipError_t s2a_launch_fwd(const void *q, const void *k, const void *v,
                           void *o, bool o_f32, float *lse, int D,

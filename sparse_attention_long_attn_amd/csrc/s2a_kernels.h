@@ -6,7 +6,7 @@
 
 struct S2AParams;
 
-int s2a_fwd_tile_rows();  // query rows per forward workgroup
+int s2a_fwd_tile_rows(int D);  // query rows per forward workgroup
 
 hipError_t s2a_launch_fwd(const void *q, const void *k, const void *v,
                           void *o, bool o_f32, float *lse, int D,

@@ -51,6 +51,8 @@ struct TileLoader {
   int row[IPW];     // tile row filled by this lane in instruction i
   int coff[IPW];    // element offset of its logical chunk within the row
   int ldsb[IPW];    // wave's LDS byte offset of instruction i (uniform)
+  unsigned boff[IPW];  // byte offset of that chunk from the tile's first
+                       // row when rows are rs elements apart (see init_rs)
 
   __device__ void init(int w, int lane) {
 #pragma unroll
@@ -60,15 +62,25 @@ struct TileLoader {
       row[i] = r;
       coff[i] = (pc ^ T::swz(r)) * 8;
       ldsb[i] = (w * IPW + i) * 64 * 16;
+      boff[i] = 0;
     }
   }
-
-  // Rows are slots s0 + row of a group; all valid and contiguous from
-  // global row pointer g0 (element pointer of slot s0's row, head h).
-  __device__ void fast(const bf16_t *g0, size_t rs, char *lds) const {
+  // Precompute the byte offsets used by fast_s(): row < ROWS <= 128 and
+  // rs = H*D, so they fit in 32 bits while H*D stays below 2^24.
+  __device__ void init_rs(size_t rs) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i)
-      g2lds16(g0 + (size_t)row[i] * rs + coff[i], lds + ldsb[i]);
+      boff[i] = (unsigned)(row[i] * rs + coff[i]) * 2u;
+  }
+
+  // Rows are slots s0 + row of a group, all valid and contiguous from the
+  // wave-uniform row pointer g0 (slot s0's row, head h): global_load_lds
+  // with a scalar base and a 32-bit per-lane offset, so no per-lane 64-bit
+  // addresses stay live across a loop.
+  __device__ void fast_s(const bf16_t *g0, char *lds) const {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      g2lds16((const char *)g0 + boff[i], lds + ldsb[i]);
   }
 
   // General rows: slot s0 + row of the group (base, glen); rows outside
@@ -78,13 +90,17 @@ struct TileLoader {
                           int s0, int N, int L, char *lds) const {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int s = s0 + row[i];
+      // opaque copies keep the compiler from hoisting per-lane 64-bit
+      // addresses of this (rare) path out of the caller's loop
+      int r = row[i], co = coff[i];
+      asm volatile("" : "+v"(r), "+v"(co));
+      const int s = s0 + r;
       int pos = 0;
       if (s < glen) {
         pos = s2a_slot_pos(base, s, N);
         if (pos >= L) pos = 0;
       }
-      g2lds16(gbh + (size_t)pos * rs + coff[i], lds + ldsb[i]);
+      g2lds16(gbh + (size_t)pos * rs + co, lds + ldsb[i]);
     }
   }
 };

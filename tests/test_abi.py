@@ -65,6 +65,7 @@ def call_bwd(**kw):
     (dict(B=0), _lib.S2A_EINVAL),
     (dict(D=24), _lib.S2A_EUNSUPPORTED),
     (dict(D=256), _lib.S2A_EUNSUPPORTED),
+    (dict(H=1 << 17, D=128), _lib.S2A_EUNSUPPORTED),   # H*D = 2^24
     (dict(), _lib.S2A_EINVAL),          # valid shape, NULL pointers
 ])
 @pytest.mark.parametrize("call", [call_fwd, call_bwd])

@@ -30,6 +30,9 @@ CASES = [
     (1, 640, 4, 32, 320, 555, 1),
     (1, 512, 4, 128, 128, 512, 0),    # shift 0: plain grouping
     (1, 4096, 2, 128, 1024, 3999, 1),
+    (1, 2304, 2, 128, 384, 2250, 1),   # groups not a multiple of 256 rows
+    (2, 192, 2, 128, 96, 190, 1),      # groups shorter than one key tile
+    (1, 8192, 2, 128, 2048, 8000, 1),  # many tiles per group, padded
 ]
 
 
@@ -107,6 +110,34 @@ def test_bf16_output_option():
     # bf16 output adds at most half a bf16 ulp (2^-6 for |o| < 8)
     compare("o_bf16", o.float().cpu().numpy(), ro, valid_rows=L,
             atol_max=ATOL_MAX + 2.0 ** -6)
+    compare_lse(lse.cpu().numpy(), rlse, L)
+
+
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT])
+def test_forward_large_logit_growth(boundary):
+    # Keys from slot 100 of every group on are scaled by 30, so a row's
+    # running max grows by far more than the forward's lazy-rescale
+    # threshold after its first key blocks: the O rescale path must run.
+    B, N, H, D, G, L = 1, 1024, 2, 128, 512, 1000
+    bits = syn.make_inputs(77, boundary, B, N, H, D)
+    kf = syn.bf16_bits_to_f64(bits["k"]).astype(np.float32)
+    slot = np.arange(N) % G
+    kf[:, slot >= 100] *= 30.0
+    kbits = syn.f32_to_bf16_bits(kf)
+    q, k, v = to_dev(bits["q"]), to_dev(kbits), to_dev(bits["v"])
+    sc = scale_for(D)
+    o, lse = s2a.fwd(q, k, v, G=G, boundary=boundary, valid_len=L, scale=sc)
+    torch.cuda.synchronize()
+    qf, vf = syn.bf16_bits_to_f64(bits["q"]), syn.bf16_bits_to_f64(bits["v"])
+    ro, rlse = oracle.forward(qf, syn.bf16_bits_to_f64(kbits), vf, G, G // 2,
+                              boundary, L, sc)
+    assert np.nanmax(rlse[..., :L]) > 40.0   # the growth really happened
+    # With a near one-hot softmax the bf16 rounding of P (2^-9 relative)
+    # no longer averages out: |dO| <= 2^-9 max|v| + 2^-9 |O| (numerator and
+    # normaliser), so the bound is 2^-8 max|v|.  A missing or wrong rescale
+    # would be off by factors of 2^60, not by 1e-2.
+    tol = 2.0 ** -8 * float(np.abs(vf).max())
+    compare("o", o.cpu().numpy(), ro, valid_rows=L, atol_max=tol)
     compare_lse(lse.cpu().numpy(), rlse, L)
 
 
