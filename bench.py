@@ -40,6 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line, time the ratio sweep "
+                         "B=2 N=12288 H=32 D=128 for every G with shift 0 and "
+                         "shift G/2 under each boundary variant (one JSON line "
+                         "per entry)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a plain copy "
                          "kernel of known size, to calibrate HBM counters)")
@@ -104,6 +109,68 @@ def cpu_baseline(cfg):
                       f"G={G} wrap: {pairs} allowed pairs"}
 
 
+SWEEP_GS = (12288, 6144, 3072, 2048, 1536)
+
+
+def sweep(args):
+    """Shift ablation over the group-ratio sweep: the same step (forward,
+    preprocess, dK/dV, dQ) timed with HIP events for shift 0 (plain
+    grouping) and shift G/2 under each boundary variant."""
+    import torch
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    from sparse_attention_long_attn_amd import work
+    B, N, H, D = 2, 12288, 32, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ins = syn.make_inputs(4, 0, B, N, H, D, with_do=True, L=N)
+    q, k, v, do = (torch.from_numpy(ins[t].view("int16")).view(torch.bfloat16)
+                   .to(dev) for t in ("q", "k", "v", "do"))
+    del ins
+    o = torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+                  for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    names = {syn.WRAP: "wrap", syn.SPLIT: "split", syn.CYCLIC: "cyclic"}
+    for G in SWEEP_GS:
+        for shift, bnd in ((0, syn.SPLIT), (G // 2, syn.SPLIT),
+                           (G // 2, syn.WRAP), (G // 2, syn.CYCLIC)):
+            kw = dict(G=G, shift=shift, boundary=bnd, valid_len=N)
+
+            def step():
+                s2a.fwd(q, k, v, o=o, lse=lse, **kw)
+                s2a.bwd_preprocess(o, do, delta)
+                s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
+                s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+
+            for _ in range(args.warmup):
+                step()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            f_fwd, f_bwd = work.useful_flops(B, N, H, D, G, shift, bnd, N)
+            pairs = work.total_pairs(B, N, H, G, shift, bnd, N)
+            print(json.dumps({
+                "metric": "S2-Attn fwd+bwd useful TFLOP/s, ratio sweep",
+                "value": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 2),
+                "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+                "steps": args.steps, "warmup": args.warmup,
+                "config": {"workload": f"B={B} N={N} H={H} D={D} G={G} "
+                                       f"shift={shift} {names[bnd]}",
+                           "group": G, "shift": shift,
+                           "boundary": names[bnd], "allowed_pairs": pairs,
+                           "ratio_to_full_causal": round(
+                               pairs / (B * H * N * (N + 1) / 2), 4)},
+            }), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -112,6 +179,10 @@ def main():
               "path (heads shard with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
     import synthetic as syn

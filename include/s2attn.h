@@ -7,16 +7,23 @@
  * of G tokens and each group runs causal attention on its own.  Heads
  * [0, H/2) group on the original boundaries; heads [H/2, H) group after a
  * shift of s = G/2 tokens and their outputs land back on the original
- * positions.  Two boundary variants of the shifted heads exist:
+ * positions.  Three boundary variants of the shifted heads exist:
  *
- *   S2A_WRAP  -- the original roll: the rolled layout is cut into N/G
- *                groups, so the last group holds positions
- *                [N-s .. N-1, 0 .. s-1] with the causal triangle taken in
- *                that order (queries 0..s-1 read keys N-s..N-1);
- *   S2A_SPLIT -- the strict-causal variant: groups [0, s), [s+kG, s+(k+1)G)
- *                for k = 0..N/G-2, and [N-s, N).
+ *   S2A_WRAP   -- the original roll: the rolled layout is cut into N/G
+ *                 groups, so the last group holds positions
+ *                 [N-s .. N-1, 0 .. s-1] with the causal triangle taken in
+ *                 that order (queries 0..s-1 read keys N-s..N-1);
+ *   S2A_SPLIT  -- the strict-causal variant: groups [0, s),
+ *                 [s+kG, s+(k+1)G) for k = 0..N/G-2, and [N-s, N);
+ *   S2A_CYCLIC -- the cyclic partition of WRAP with the causal order taken
+ *                 on original positions: the last group is
+ *                 [0 .. s-1, N-s .. N-1] in that order, so queries
+ *                 N-s..N-1 read keys 0..s-1 and nothing reads a later
+ *                 position.
  *
- * Both come from §1's paragraph on cyclic shifts (Figure 1, right and left).
+ * The first two come from §1's paragraph on cyclic shifts (Figure 1, right
+ * and left), the third from §2.2 ("平移分组究竟改变了怎样的信息图"), the
+ * mask M^(s) with j <= i and floor(((i+s) mod N)/G) equal for i and j.
  * A padded tail is masked inside every softmax: keys at positions >= the
  * valid length never contribute (§1, paragraph on padding to whole groups).
  * If N/G == 1 the shift has no effect (both head classes are plain causal
@@ -54,7 +61,7 @@ typedef enum {
   S2A_EHIP = 3          /* a HIP launch failed                            */
 } s2a_status;
 
-typedef enum { S2A_WRAP = 0, S2A_SPLIT = 1 } s2a_boundary;
+typedef enum { S2A_WRAP = 0, S2A_SPLIT = 1, S2A_CYCLIC = 2 } s2a_boundary;
 typedef enum { S2A_BF16 = 0, S2A_F32 = 1 } s2a_dtype;
 
 /*
@@ -137,8 +144,10 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
  *   src[c*N + r]  = original position held at row r.
  * Class 0 groups are [kG, (k+1)G).  Class 1 follows `boundary` (WRAP:
  * N/G groups of the layout rolled left by s; SPLIT: N/G + 1 groups, the
- * first and last of length s).  The maps do not depend on valid_len (pad
- * first, then shift), which is only validated.
+ * first and last of length s; CYCLIC: the groups of WRAP, the last one in
+ * position order, so its slots hold 0..s-1 and then N-s..N-1).  The maps do
+ * not depend on valid_len (pad first, then shift), which is only
+ * validated.
  */
 s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
                             int valid_len, int *gid, int *slot, int *src,

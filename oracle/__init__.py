@@ -24,7 +24,7 @@ textbook causal attention brute-forced in Python loops, a library SDPA
 routine on unpadded segments, central finite differences, invariants).
 """
 from .s2attn_oracle import (  # noqa: F401
-    WRAP, SPLIT, OracleError, effective_shift, validate, group_maps_a,
+    WRAP, SPLIT, CYCLIC, OracleError, effective_shift, validate, group_maps_a,
     group_maps_b, adjacency_block, adjacency_dense, allowed_pairs, forward,
     backward, forward_segments, backward_segments, segments,
 )

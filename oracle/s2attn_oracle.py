@@ -31,6 +31,7 @@ import numpy as np
 
 WRAP = 0
 SPLIT = 1
+CYCLIC = 2
 
 
 class OracleError(ValueError):
@@ -55,8 +56,8 @@ def validate(N: int, H: int, D: int, G: int, shift: int, boundary: int,
         raise OracleError("valid length must be in [1, N]")
     if shift not in (0, G // 2):
         raise OracleError("shift must be 0 or G/2")
-    if boundary not in (WRAP, SPLIT):
-        raise OracleError("boundary must be WRAP or SPLIT")
+    if boundary not in (WRAP, SPLIT, CYCLIC):
+        raise OracleError("boundary must be WRAP, SPLIT or CYCLIC")
 
 
 def effective_shift(N: int, G: int, shift: int) -> int:
@@ -86,7 +87,11 @@ def group_maps_a(N: int, G: int, shift: int, boundary: int):
              wrapped group [N-s .. N-1, 0 .. s-1] ([LL] §1, N=8 example);
       SPLIT: gid = b'(x) + 1 in [0, N/G]; group 0 is the short head [0, s),
              group N/G the short tail [N-s, N); slots count from each
-             group's first position (lower bound of N_1(i)).
+             group's first position (lower bound of N_1(i));
+      CYCLIC: the partition floor(((x + s) mod N)/G) of the mask M_h^(s)
+             ([LL] §2.2), renumbered so that the group holding both ends
+             is the last one, as in WRAP; a slot is the rank of the
+             position inside its group (causal order is original order).
     The map does not depend on the valid length (pad first, then shift)."""
     x = np.arange(N, dtype=np.int64)
     s = effective_shift(N, G, shift)
@@ -100,6 +105,15 @@ def group_maps_a(N: int, G: int, shift: int, boundary: int):
         p = np.mod(x - s, N)
         gid[1], slot[1] = p // G, p % G
         src[1] = np.mod(x + s, N)          # rolled row r holds x = r + s
+    elif boundary == CYCLIC:
+        M = N // G
+        g = np.mod(np.mod(x + s, N) // G - 1, M)
+        order = np.lexsort((x, g))         # by group, then by position
+        gid[1] = g
+        src[1] = x[order]
+        rank = np.empty(N, np.int64)
+        rank[order] = np.arange(N) - g[order] * G
+        slot[1] = rank
     else:
         g = np.floor_divide(x - s, G) + 1
         start = np.maximum(0, s + (g - 1) * G)
@@ -120,7 +134,9 @@ def adjacency_block(cls: int, rows: np.ndarray, N: int, G: int, shift: int,
     Class 1 WRAP: with p(x) = (x - s) mod N, floor(p(i)/G) == floor(p(j)/G)
     and p(j) <= p(i): the triangle is taken in rolled order, so queries
     0..s-1 read keys N-s..N-1 ([LL] §1, cyclic-shift paragraph).
-    Both: i < L and j < L (padding never enters the softmax)."""
+    Class 1 CYCLIC: floor(((i+s) mod N)/G) == floor(((j+s) mod N)/G) and
+    j <= i ([LL] §2.2, mask M_h^(s)).
+    All: i < L and j < L (padding never enters the softmax)."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(N, dtype=np.int64)[None, :]
     s = effective_shift(N, G, shift) if cls == 1 else 0
@@ -128,6 +144,8 @@ def adjacency_block(cls: int, rows: np.ndarray, N: int, G: int, shift: int,
         a = (i // G == j // G) & (j <= i)
     elif boundary == SPLIT:
         a = (np.floor_divide(i - s, G) == np.floor_divide(j - s, G)) & (j <= i)
+    elif boundary == CYCLIC:
+        a = (np.mod(i + s, N) // G == np.mod(j + s, N) // G) & (j <= i)
     else:
         pi, pj = np.mod(i - s, N), np.mod(j - s, N)
         a = (pi // G == pj // G) & (pj <= pi)
@@ -264,7 +282,9 @@ def segments(N: int, G: int, shift: int, boundary: int):
     forward_flashattn / forward_noflashattn):
       class 0            : arange(N) cut into N/G rows of G;
       class 1, WRAP      : np.roll(arange(N), -s) cut into N/G rows of G;
-      class 1, SPLIT     : arange(N) split at s, s+G, ..., N-s."""
+      class 1, SPLIT     : arange(N) split at s, s+G, ..., N-s;
+      class 1, CYCLIC    : the rows of WRAP, each sorted by position (causal
+                           order on original positions, [LL] §2.2)."""
     s = effective_shift(N, G, shift)
     M = N // G
     pos = np.arange(N, dtype=np.int64)
@@ -273,6 +293,8 @@ def segments(N: int, G: int, shift: int, boundary: int):
         c1 = [seg.copy() for seg in c0]
     elif boundary == WRAP:
         c1 = list(np.roll(pos, -s).reshape(M, G))
+    elif boundary == CYCLIC:
+        c1 = [np.sort(row) for row in np.roll(pos, -s).reshape(M, G)]
     else:
         cuts = [s + t * G for t in range(M)]
         c1 = np.split(pos, cuts)

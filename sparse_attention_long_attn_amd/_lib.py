@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libs2attn.so")
 
 S2A_OK, S2A_EINVAL, S2A_EUNSUPPORTED, S2A_EHIP = 0, 1, 2, 3
-S2A_WRAP, S2A_SPLIT = 0, 1
+S2A_WRAP, S2A_SPLIT, S2A_CYCLIC = 0, 1, 2
 S2A_BF16, S2A_F32 = 0, 1
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",

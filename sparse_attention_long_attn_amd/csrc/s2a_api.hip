@@ -37,8 +37,9 @@ s2a_status check_shape(int B, int N, int H, int D, int G, int shift,
     return fail(S2A_EINVAL, "valid_len=%lld outside [1, N=%lld]", valid_len, N);
   if (shift != 0 && shift != G / 2)
     return fail(S2A_EINVAL, "shift=%lld must be 0 or G/2=%lld", shift, G / 2);
-  if (boundary != S2A_WRAP && boundary != S2A_SPLIT)
-    return fail(S2A_EINVAL, "boundary=%lld is neither WRAP nor SPLIT", boundary);
+  if (boundary != S2A_WRAP && boundary != S2A_SPLIT && boundary != S2A_CYCLIC)
+    return fail(S2A_EINVAL, "boundary=%lld is not WRAP, SPLIT or CYCLIC",
+                boundary);
   if (D != 16 && D != 32 && D != 64 && D != 128)
     return fail(S2A_EUNSUPPORTED, "head width D=%lld not in {16,32,64,128}", D);
   // Offsets of a row are formed in 64 bits; positions and grid sizes in 32;

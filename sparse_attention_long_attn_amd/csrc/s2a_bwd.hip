@@ -48,15 +48,6 @@ struct BwdDims {
   static constexpr int CPR = DP / 8;      // 16-byte chunks per row
 };
 
-// True if the slots [k0, kend) of a group hold a position >= L.
-__device__ __forceinline__ bool range_has_padding(int base, int k0, int kend,
-                                                  int N, int L) {
-  if (L >= N) return false;
-  const int first = s2a_slot_pos(base, k0, N);
-  const int last = s2a_slot_pos(base, kend - 1, N);
-  return last >= first ? last >= L : true;  // a wrapped range holds N-1
-}
-
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O)
 // ---------------------------------------------------------------------------
@@ -106,7 +97,8 @@ __global__ __launch_bounds__(256) void s2a_bwd_pre_kernel(
 // (batch, head, group) unit get workgroup ids equal mod 8, so they run on
 // one XCD and share its L2.
 struct UnitTile {
-  int b, h, cls, base, glen, tile;
+  S2ARun run;
+  int b, h, cls, glen, tile;
   bool ok;
 };
 
@@ -125,7 +117,7 @@ __device__ __forceinline__ UnitTile decode(const S2AParams &p, bool reverse) {
   r.h = bh % p.H;
   r.b = bh / p.H;
   r.cls = r.h >= (p.H >> 1);
-  r.ok = s2a_group(p.g, r.cls, gi, r.base, r.glen);
+  r.ok = s2a_group(p.g, r.cls, gi, r.run, r.glen);
   return r;
 }
 
@@ -156,7 +148,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
 
   const UnitTile ut = decode(p, false);  // first key tile (longest walk) first
   if (!ut.ok) return;
-  const int base = ut.base, glen = ut.glen;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
   const int k0 = ut.tile * KV_BK;
   if (k0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -169,7 +162,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + l32;
   const bool kin = key < glen;
-  const int kpos = kin ? s2a_slot_pos(base, key, N) : 0;
+  const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
   const bool wave_keys_valid = __all(kvalid);
 
@@ -200,7 +193,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       const int qsl = q0 + r;
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
       if (qsl < glen && ch * 8 < D) {
-        const int qp = s2a_slot_pos(base, qsl, N);
+        const int qp = run.pos(qsl);
         if (qp < L) {
           const size_t off = boff + (size_t)qp * rs + ch * 8;
           qv = *(const u32x4 *)(q + off);
@@ -215,7 +208,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       l2st = INFINITY;
       dlst = 0.f;
       if (qsl < glen) {
-        const int qp = s2a_slot_pos(base, qsl, N);
+        const int qp = run.pos(qsl);
         if (qp < L) {
           l2st = lse[lrow + qp] * S2A_LOG2E;
           dlst = delta[lrow + qp];
@@ -368,7 +361,8 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
 
   const UnitTile ut = decode(p, true);  // heaviest (last) query tile first
   if (!ut.ok) return;
-  const int base = ut.base, glen = ut.glen;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
   const int q0 = ut.tile * DQ_BQ;
   if (q0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -380,7 +374,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
   // This lane's query (one column of S^T, dP^T, dS^T).
   const int qslot = q0 + 32 * w + l32;
   const bool qin = qslot < glen;
-  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
@@ -409,7 +403,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
       const int ks = k0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (c < TCH && ks < glen && ch * 8 < D) {
-        const int kp = s2a_slot_pos(base, ks, N);
+        const int kp = run.pos(ks);
         if (kp < L) {
           const size_t off = boff + (size_t)kp * rs + ch * 8;
           kv = *(const u32x4 *)(k + off);
@@ -475,7 +469,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
       // dS^T; element i of block kb is key k0 + 32kb + 8(i/4) + 4hf + i%4.
       const int kstop = min(k0 + DQ_BK, glen);
       const bool edge = (k0 + DQ_BK - 1 > wq_lo) || (k0 + DQ_BK > glen) ||
-                        range_has_padding(base, k0, kstop, N, L);
+                        s2a_range_has_padding(run, k0, kstop, N, L);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -483,7 +477,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
           float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
           if (edge) {
             const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!(ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L))
+            if (!(ks <= qslot && ks < glen && run.pos(ks) < L))
               pp = 0.f;
           }
           dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
@@ -553,7 +547,8 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 
   const UnitTile ut = decode(p, true);
   if (!ut.ok) return;
-  const int base = ut.base, glen = ut.glen;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
   const int q0 = ut.tile * DQ_BQ;
   if (q0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -565,7 +560,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 
   const int qslot = q0 + 32 * w + l32;
   const bool qin = qslot < glen;
-  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
@@ -590,13 +585,13 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   ld.init_rs(rs);
   auto issue = [&](int k0, int buf) {
     char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
-    if (tile_plain(base, glen, k0, DQ_BK, N, L)) {
-      const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
+    if (tile_plain(run, glen, k0, DQ_BK, L)) {
+      const size_t r0 = (size_t)run.pos(k0) * rs;
       ld.fast_s(kbh + r0, kd);
       ld.fast_s(vbh + r0, vd);
     } else {
-      ld.general(kbh, rs, base, glen, k0, N, L, kd);
-      ld.general(vbh, rs, base, glen, k0, N, L, vd);
+      ld.general(kbh, rs, run, glen, k0, L, kd);
+      ld.general(vbh, rs, run, glen, k0, L, vd);
     }
   };
   // (rows trow and trow + 8 of a 16-row step have different swizzles)
@@ -655,7 +650,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
         }
       }
       const bool edge = (k0 + DQ_BK - 1 > wq_lo) ||
-                        !tile_plain(base, glen, k0, DQ_BK, N, L);
+                        !tile_plain(run, glen, k0, DQ_BK, L);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -663,25 +658,40 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
           float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
           if (edge) {
             const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!(ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L))
+            if (!(ks <= qslot && ks < glen && run.pos(ks) < L))
               pp = 0.f;
           }
           dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
         }
+      // dQ^T += K^T dS^T.  On edge tiles (the diagonal, where rows see few
+      // keys and |dS| is largest) dS goes in as bf16 hi + lo parts, which
+      // removes most of the bf16 rounding of dS from those rows' error.
+      // pass 0: dS rounded to bf16; pass 1 (edge tiles only): the rounding
+      // residual dS - bf16(dS), also in bf16
+      auto dq_product = [&](auto lo_tag) {
+        constexpr bool LO = decltype(lo_tag)::value;
 #pragma unroll
-      for (int ks = 0; ks < DQ_BK / 16; ++ks) {
-        const f32x16 &dp = dpacc[ks >> 1];
-        const int e0 = 8 * (ks & 1);
-        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
-                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
-        const char *kr = Kb + 16 * ks * T::ROWB;
+        for (int ks = 0; ks < DQ_BK / 16; ++ks) {
+          const f32x16 &dp = dpacc[ks >> 1];
+          const int e0 = 8 * (ks & 1);
+          bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
+                                dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+          if constexpr (LO)
+            sb = to_bf16x8(dp[e0] - (float)sb[0], dp[e0 + 1] - (float)sb[1],
+                           dp[e0 + 2] - (float)sb[2], dp[e0 + 3] - (float)sb[3],
+                           dp[e0 + 4] - (float)sb[4], dp[e0 + 5] - (float)sb[5],
+                           dp[e0 + 6] - (float)sb[6], dp[e0 + 7] - (float)sb[7]);
+          const char *kr = Kb + 16 * ks * T::ROWB;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[db])),
-                                 lds_read_tr((const bf16_t *)(kr + troff8[db])));
-          dqacc[db] = mfma32(ak, sb, dqacc[db]);
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[db])),
+                                   lds_read_tr((const bf16_t *)(kr + troff8[db])));
+            dqacc[db] = mfma32(ak, sb, dqacc[db]);
+          }
         }
-      }
+      };
+      dq_product(std::false_type{});
+      if (edge) dq_product(std::true_type{});
     }
     wait_vm_all();
     __syncthreads();
@@ -737,7 +747,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 
   const UnitTile ut = decode(p, false);
   if (!ut.ok) return;
-  const int base = ut.base, glen = ut.glen;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
   const int k0 = ut.tile * KV_BK;
   if (k0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -750,7 +761,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + l32;
   const bool kin = key < glen;
-  const int kpos = kin ? s2a_slot_pos(base, key, N) : 0;
+  const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
 
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
@@ -780,7 +791,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       l2st = INFINITY;
       dlst = 0.f;
       if (qsl < glen) {
-        const int qp = s2a_slot_pos(base, qsl, N);
+        const int qp = run.pos(qsl);
         if (qp < L) {
           l2st = lse[lrow + qp] * S2A_LOG2E;
           dlst = delta[lrow + qp];
@@ -796,13 +807,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   };
   auto issue_tile = [&](int q0, int buf) {
     char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
-    if (tile_plain(base, glen, q0, BQ, N, L)) {
-      const size_t r0 = (size_t)s2a_slot_pos(base, q0, N) * rs;
+    if (tile_plain(run, glen, q0, BQ, L)) {
+      const size_t r0 = (size_t)run.pos(q0) * rs;
       ld.fast_s(qbh + r0, qd);
       ld.fast_s(gbh + r0, gd);
     } else {
-      ld.general(qbh, rs, base, glen, q0, N, L, qd);
-      ld.general(gbh, rs, base, glen, q0, N, L, gd);
+      ld.general(qbh, rs, run, glen, q0, L, qd);
+      ld.general(gbh, rs, run, glen, q0, L, gd);
     }
   };
   // (rows trow and trow + 8 of a 16-row step have different swizzles)

@@ -18,7 +18,7 @@
 //                         P^T from the S^T accumulators (same key order)
 // and the epilogue writes O and the natural-log LSE at the rows' original
 // positions (the inverse shift costs nothing: addresses come from
-// s2a_slot_pos()).
+// the group's S2ARun).
 #include "s2a_device.h"
 #include "s2a_kernels.h"
 #include "s2a_tile.h"
@@ -39,15 +39,6 @@ struct FwdDims {
   static constexpr int DB = DP / 32;          // 32-wide blocks over d
   static constexpr int CPR = DP / 8;          // 16-byte chunks per row
 };
-
-// True if the key slots [k0, kend) of a group hold a position >= L.
-__device__ __forceinline__ bool tile_has_padding(int base, int k0, int kend,
-                                                 int N, int L) {
-  if (L >= N) return false;
-  const int first = s2a_slot_pos(base, k0, N);
-  const int last = s2a_slot_pos(base, kend - 1, N);
-  return last >= first ? last >= L : true;  // a wrapped tile holds N-1
-}
 
 template <int D, bool OF32>
 __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
@@ -79,8 +70,9 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   const int bh = u / p.ngmax;
   const int h = bh % p.H, b = bh / p.H;
   const int cls = h >= (p.H >> 1);
-  int base, glen;
-  if (!s2a_group(p.g, cls, gi, base, glen)) return;
+  S2ARun run;
+  int glen;
+  if (!s2a_group(p.g, cls, gi, run, glen)) return;
   const int q0 = tile * FWD_BQ;
   if (q0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -90,7 +82,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   // This lane's query (one column of S^T).
   const int qslot = q0 + 32 * w + l32;
   const bool qin = qslot < glen;
-  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
 
   bf16x8 qreg[Dm::KSTEPS];
@@ -116,7 +108,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
       const int ks = k0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (c < TCH && ks < glen && ch * 8 < D) {
-        const int kp = s2a_slot_pos(base, ks, N);
+        const int kp = run.pos(ks);
         if (kp < L) {
           const size_t off = boff + (size_t)kp * rs + ch * 8;
           kv = *(const u32x4 *)(k + off);
@@ -189,7 +181,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
       // Mask where the tile crosses the diagonal, the group end or padding.
       const int kstop = min(k0 + FWD_BK, glen);
       const bool edge = (k0 + FWD_BK - 1 > wq_lo) || (k0 + FWD_BK > glen) ||
-                        tile_has_padding(base, k0, kstop, N, L);
+                        s2a_range_has_padding(run, k0, kstop, N, L);
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -197,7 +189,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
           for (int i = 0; i < 16; ++i) {
             const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
             const bool ok =
-                ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
+                ks <= qslot && ks < glen && run.pos(ks) < L;
             if (!ok) sacc[kb][i] = -INFINITY;
           }
       }
@@ -317,8 +309,9 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   const int bh = u / p.ngmax;
   const int h = bh % p.H, b = bh / p.H;
   const int cls = h >= (p.H >> 1);
-  int base, glen;
-  if (!s2a_group(p.g, cls, gi, base, glen)) return;
+  S2ARun run;
+  int glen;
+  if (!s2a_group(p.g, cls, gi, run, glen)) return;
   const int q0 = tile * FWD_BQ;
   if (q0 >= glen) return;
   const int N = p.g.N, L = p.g.L;
@@ -328,7 +321,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
 
   const int qslot = q0 + 32 * w + l32;
   const bool qin = qslot < glen;
-  const int qpos = qin ? s2a_slot_pos(base, qslot, N) : 0;
+  const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
 
   bf16x8 qreg[KSTEPS];
@@ -347,13 +340,13 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   ld.init_rs(rs);
   auto issue = [&](int k0, int buf) {
     char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
-    if (tile_plain(base, glen, k0, FWD_BK, N, L)) {
-      const size_t r0 = (size_t)s2a_slot_pos(base, k0, N) * rs;
+    if (tile_plain(run, glen, k0, FWD_BK, L)) {
+      const size_t r0 = (size_t)run.pos(k0) * rs;
       ld.fast_s(kbh + r0, kd);
       ld.fast_s(vbh + r0, vd);
     } else {
-      ld.general(kbh, rs, base, glen, k0, N, L, kd);
-      ld.general(vbh, rs, base, glen, k0, N, L, vd);
+      ld.general(kbh, rs, run, glen, k0, L, kd);
+      ld.general(vbh, rs, run, glen, k0, L, vd);
     }
   };
 
@@ -415,7 +408,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
       }
 
       const bool edge = (k0 + FWD_BK - 1 > wq_lo) ||
-                        !tile_plain(base, glen, k0, FWD_BK, N, L);
+                        !tile_plain(run, glen, k0, FWD_BK, L);
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -423,7 +416,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
           for (int i = 0; i < 16; ++i) {
             const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
             const bool ok =
-                ks <= qslot && ks < glen && s2a_slot_pos(base, ks, N) < L;
+                ks <= qslot && ks < glen && run.pos(ks) < L;
             if (!ok) sacc[kb][i] = -INFINITY;
           }
       }

@@ -5,14 +5,20 @@
 // of class 1 (the second half of the heads) groups them after a shift of
 // s = G/2 (PaperTrace "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调", §1: the
 // group functions b(i) = floor(i/G) and b'(i) = floor((i - G/2)/G), and the
-// cyclic-shift paragraph for the two boundary variants).
+// cyclic-shift paragraph for the two boundary variants; §2.2 for the third).
+// The boundary variant decides the shifted class's groups and their order:
+//   WRAP    the original roll: groups [s + kG, s + (k+1)G) mod N; the last
+//           one holds N-s .. N-1 and then 0 .. s-1, in that order (the
+//           causal triangle is taken in this rolled order);
+//   SPLIT   strict causal: [0, s), [s + kG, s + (k+1)G), [N-s, N);
+//   CYCLIC  the cyclic partition of WRAP with causality on original
+//           positions (§2.2's teaching graph): the last group is ordered
+//           0 .. s-1, then N-s .. N-1, so its tail reads its head.
 //
-// Every group is described by (base, len): its slot j (0 <= j < len) holds
-// the original position base + j, reduced mod N.  The reduction only
-// matters for the wrapped group of the WRAP variant, whose slots run over
-// N-s .. N-1 and then 0 .. s-1; everywhere else base + j < N.  The kernels
-// never build a rolled copy of Q/K/V: a row's address is computed from its
-// slot with slot_pos().
+// A group is a run of slots j = 0 .. len-1 (S2ARun) whose original
+// positions form at most two increasing runs: slot j holds
+// base + j - (j >= cut ? jump : 0).  The kernels never build a rolled copy
+// of Q/K/V: a row's address is computed from its slot with pos().
 #pragma once
 
 #ifndef __HIPCC__
@@ -22,14 +28,25 @@
 
 #define S2A_BOUNDARY_WRAP 0
 #define S2A_BOUNDARY_SPLIT 1
+#define S2A_BOUNDARY_CYCLIC 2
 
 struct S2AGeom {
   int N;         // padded length
   int G;         // group length
   int s;         // effective shift (0 if shift == 0 or N == G)
   int M;         // N / G
-  int boundary;  // S2A_BOUNDARY_WRAP or S2A_BOUNDARY_SPLIT
+  int boundary;  // S2A_BOUNDARY_WRAP, _SPLIT or _CYCLIC
   int L;         // valid length
+};
+
+// Slot -> original position of one group (see the file comment).
+struct S2ARun {
+  int base;  // position of slot 0
+  int cut;   // first slot of the second run (len if there is none)
+  int jump;  // subtracted from base + j from slot cut on
+  __host__ __device__ int pos(int j) const {
+    return base + j - (j >= cut ? jump : 0);
+  }
 };
 
 // Number of groups of head class cls.
@@ -43,28 +60,43 @@ __host__ __device__ inline int s2a_max_groups(const S2AGeom &g) {
   return s2a_num_groups(g, 1);
 }
 
-// (base, len) of group gi of class cls; returns false if gi is past the
+// Run and length of group gi of class cls; returns false if gi is past the
 // last group of that class.
 __host__ __device__ inline bool s2a_group(const S2AGeom &g, int cls, int gi,
-                                          int &base, int &len) {
+                                          S2ARun &run, int &len) {
   if (gi < 0 || gi >= s2a_num_groups(g, cls)) return false;
   if (cls == 0 || g.s == 0) {
-    base = gi * g.G;
+    run = {gi * g.G, g.G, 0};
+    len = g.G;
+  } else if (g.boundary == S2A_BOUNDARY_SPLIT) {
+    const int base = gi == 0 ? 0 : g.s + (gi - 1) * g.G;
+    len = (gi == 0 || gi == g.M) ? g.s : g.G;
+    run = {base, len, 0};
+  } else if (gi < g.M - 1) {  // WRAP and CYCLIC agree away from the wrap
+    run = {gi * g.G + g.s, g.G, 0};
     len = g.G;
   } else if (g.boundary == S2A_BOUNDARY_WRAP) {
-    base = gi * g.G + g.s;  // rolled left by s: slot j of group gi holds
-    len = g.G;              // position (gi*G + s + j) mod N
+    run = {g.N - g.s, g.s, g.N};  // N-s .. N-1, then 0 .. s-1
+    len = g.G;
   } else {
-    base = gi == 0 ? 0 : g.s + (gi - 1) * g.G;
-    len = (gi == 0 || gi == g.M) ? g.s : g.G;
+    run = {0, g.s, 2 * g.s - g.N};  // 0 .. s-1, then N-s .. N-1
+    len = g.G;
   }
   return true;
 }
 
-// Original position of slot j of a group with the given base.
-__host__ __device__ inline int s2a_slot_pos(int base, int j, int N) {
-  int p = base + j;
-  return p >= N ? p - N : p;
+// True if a slot of [j0, j1) (j0 < j1) holds a position >= L.  The largest
+// position of the range is the last slot of one of its runs.
+__host__ __device__ inline bool s2a_range_has_padding(const S2ARun &run,
+                                                      int j0, int j1, int N,
+                                                      int L) {
+  if (L >= N) return false;
+  int mx = run.pos(j1 - 1);
+  if (j0 < run.cut && j1 > run.cut) {
+    const int m1 = run.pos(run.cut - 1);
+    mx = m1 > mx ? m1 : mx;
+  }
+  return mx >= L;
 }
 
 // Inverse map: group and slot of original position x in class cls.
@@ -73,23 +105,28 @@ __host__ __device__ inline void s2a_locate(const S2AGeom &g, int cls, int x,
   if (cls == 0 || g.s == 0) {
     gi = x / g.G;
     slot = x - gi * g.G;
-  } else if (g.boundary == S2A_BOUNDARY_WRAP) {
-    int p = x - g.s;
+  } else if (g.boundary == S2A_BOUNDARY_SPLIT) {
+    if (x < g.s) {
+      gi = 0;
+      slot = x;
+    } else {
+      gi = (x - g.s) / g.G + 1;
+      slot = x - (g.s + (gi - 1) * g.G);
+    }
+  } else {
+    int p = x - g.s;  // rolled index
     if (p < 0) p += g.N;
     gi = p / g.G;
     slot = p - gi * g.G;
-  } else if (x < g.s) {
-    gi = 0;
-    slot = x;
-  } else {
-    gi = (x - g.s) / g.G + 1;
-    slot = x - (g.s + (gi - 1) * g.G);
+    if (g.boundary == S2A_BOUNDARY_CYCLIC && gi == g.M - 1)
+      slot = x < g.s ? x : x - (g.N - g.s) + g.s;  // position order
   }
 }
 
 // Row r of the regrouped layout (the groups of a class laid end to end in
-// group order): its group gi and slot j.  For the WRAP variant the rows are
-// the rolled layout; for SPLIT and for class 0 they are the original order.
+// group order): its group gi and slot j.  For WRAP the rows are the rolled
+// layout (CYCLIC: the same, with the last group in position order); for
+// SPLIT and for class 0 they are the original order.
 __host__ __device__ inline void s2a_row_locate(const S2AGeom &g, int cls,
                                                int r, int &gi, int &j) {
   if (cls == 1 && g.s > 0 && g.boundary == S2A_BOUNDARY_SPLIT) {

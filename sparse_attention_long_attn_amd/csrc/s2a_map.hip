@@ -16,10 +16,11 @@ __global__ __launch_bounds__(256) void s2a_map_kernel(S2AGeom g, int *gid,
     s2a_locate(g, cls, x, gi, sl);
     gid[cls * g.N + x] = gi;
     slot[cls * g.N + x] = sl;
-    int gr, j, base, len;
+    int gr, j, len;
+    S2ARun run;
     s2a_row_locate(g, cls, x, gr, j);  // x read as a row of the layout
-    s2a_group(g, cls, gr, base, len);
-    src[cls * g.N + x] = s2a_slot_pos(base, j, g.N);
+    s2a_group(g, cls, gr, run, len);
+    src[cls * g.N + x] = run.pos(j);
   }
 }
 

@@ -83,11 +83,11 @@ struct TileLoader {
       g2lds16((const char *)g0 + boff[i], lds + ldsb[i]);
   }
 
-  // General rows: slot s0 + row of the group (base, glen); rows outside
+  // General rows: slot s0 + row of the group (run, glen); rows outside
   // the group or at positions >= L read position 0 of the same (b, h)
   // instead (finite data that the kernels mask out).
-  __device__ void general(const bf16_t *gbh, size_t rs, int base, int glen,
-                          int s0, int N, int L, char *lds) const {
+  __device__ void general(const bf16_t *gbh, size_t rs, const S2ARun &run,
+                          int glen, int s0, int L, char *lds) const {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       // opaque copies keep the compiler from hoisting per-lane 64-bit
@@ -97,7 +97,7 @@ struct TileLoader {
       const int s = s0 + r;
       int pos = 0;
       if (s < glen) {
-        pos = s2a_slot_pos(base, s, N);
+        pos = run.pos(s);
         if (pos >= L) pos = 0;
       }
       g2lds16(gbh + (size_t)pos * rs + co, lds + ldsb[i]);
@@ -106,13 +106,13 @@ struct TileLoader {
 };
 
 // The tile [s0, s0 + rows) of a group is "plain" when every slot is inside
-// the group, the positions do not wrap and all are below L: then rows are
+// the group, inside one run, and at a position below L: then its rows are
 // contiguous in memory from slot s0's position.
-__device__ __forceinline__ bool tile_plain(int base, int glen, int s0,
-                                           int rows, int N, int L) {
+__device__ __forceinline__ bool tile_plain(const S2ARun &run, int glen,
+                                           int s0, int rows, int L) {
   if (s0 + rows > glen) return false;
-  const int p0 = s2a_slot_pos(base, s0, N);
-  return p0 + rows <= L;  // L <= N, so this also rules out a wrap
+  if (s0 < run.cut && s0 + rows > run.cut) return false;
+  return run.pos(s0) + rows <= L;
 }
 
 __device__ __forceinline__ void wait_vm_all() {

@@ -14,14 +14,16 @@ import torch
 from . import _lib
 
 BOUNDARIES = {"wrap": _lib.S2A_WRAP, "split": _lib.S2A_SPLIT,
-              _lib.S2A_WRAP: _lib.S2A_WRAP, _lib.S2A_SPLIT: _lib.S2A_SPLIT}
+              "cyclic": _lib.S2A_CYCLIC, _lib.S2A_WRAP: _lib.S2A_WRAP,
+              _lib.S2A_SPLIT: _lib.S2A_SPLIT, _lib.S2A_CYCLIC: _lib.S2A_CYCLIC}
 
 
 def _boundary(b) -> int:
     try:
         return BOUNDARIES[b]
     except KeyError:
-        raise ValueError(f"boundary must be 'wrap' or 'split', got {b!r}")
+        raise ValueError(f"boundary must be 'wrap', 'split' or 'cyclic', "
+                         f"got {b!r}")
 
 
 def _ptr(t: torch.Tensor) -> int:

@@ -9,34 +9,30 @@ pair for the forward (2D for QK^T, 2D for PV) and 10*D for the backward.
 """
 from __future__ import annotations
 
-WRAP, SPLIT = 0, 1
+WRAP, SPLIT, CYCLIC = 0, 1, 2
 
 
 def _groups(N, G, shift, boundary, cls):
-    """(start position, length, wrapped) of each group of a head class."""
+    """Each group of a head class as its runs of consecutive positions,
+    [(first, end), ...] in group (causal) order."""
     M = N // G
     s = 0 if M == 1 else shift
     if cls == 0 or s == 0:
-        return [(g * G, G) for g in range(M)]
-    if boundary == WRAP:
-        return [(g * G + s, G) for g in range(M)]
-    return [(0, s)] + [(s + g * G, G) for g in range(M - 1)] + [(N - s, s)]
+        return [[(g * G, g * G + G)] for g in range(M)]
+    if boundary == SPLIT:
+        return ([[(0, s)]] + [[(s + g * G, s + g * G + G)] for g in range(M - 1)]
+                + [[(N - s, N)]])
+    inner = [[(g * G + s, g * G + s + G)] for g in range(M - 1)]
+    if boundary == WRAP:                 # rolled order: N-s..N-1, 0..s-1
+        return inner + [[(N - s, N), (0, s)]]
+    return inner + [[(0, s), (N - s, N)]]  # CYCLIC: position order
 
 
-def _pairs_in_group(base, n, N, L):
-    """Causal pairs among the valid members of a group whose slot j holds
-    position (base + j) mod N."""
-    # valid slots form at most two runs; pairs = sum over valid slots j of
-    # (number of valid slots <= j)
+def _pairs_in_group(runs, L):
+    """Causal pairs among the valid members of a group given as runs."""
+    # pairs = sum over valid slots j of (number of valid slots <= j)
     tot = 0
     cnt = 0
-    # walk runs rather than slots: slots [0, n) map to [base, base+n) mod N
-    runs = []
-    if base + n <= N:
-        runs.append((base, base + n))
-    else:
-        runs.append((base, N))
-        runs.append((0, base + n - N))
     for a, b in runs:
         v = max(0, min(b, L) - a)      # valid positions of the run
         tot += v * cnt + v * (v + 1) // 2
@@ -48,8 +44,8 @@ def allowed_pairs(N, G, shift, boundary, L):
     """Allowed (query, key) pairs per head of class 0 and class 1."""
     out = []
     for cls in (0, 1):
-        out.append(sum(_pairs_in_group(b, n, N, L)
-                       for b, n in _groups(N, G, shift, boundary, cls)))
+        out.append(sum(_pairs_in_group(runs, L)
+                       for runs in _groups(N, G, shift, boundary, cls)))
     return tuple(out)
 
 

@@ -21,6 +21,7 @@ import numpy as np
 
 WRAP = 0
 SPLIT = 1
+CYCLIC = 2
 
 # Workload shapes (Llama-2-7B attention layer: 32 heads of width 128).
 # Each entry: B, N (padded length), H, D, list of G, list of boundary

@@ -109,7 +109,7 @@ def test_strerror():
 @pytest.mark.parametrize("N,G,L", [(64, 16, 64), (64, 16, 50), (64, 16, 5),
                                    (48, 12, 37), (96, 32, 81), (128, 128, 100),
                                    (256, 64, 200), (256, 64, 250)])
-@pytest.mark.parametrize("boundary", [0, 1])
+@pytest.mark.parametrize("boundary", [0, 1, 2])
 @pytest.mark.parametrize("half", [0, 1])
 def test_work_pairs_match_oracle_enumeration(N, G, L, boundary, half):
     shift = half * G // 2

@@ -7,9 +7,9 @@ recomputes sampled outputs it can produce exactly on their own:
   slots of a group those are exactly the last R slots of the group.
 
 Samples cover one head of each class, the first, a middle and the last
-group (the wrapped group under WRAP, the short tail under SPLIT), the
-first and last R slots of each, and for padded inputs the slots around the
-valid-length boundary and the wrap point."""
+group (the wrapped group under WRAP and CYCLIC, the short tail under
+SPLIT), the first and last R slots of each, and for padded inputs the slots
+around the valid-length boundary and wherever a group's positions jump."""
 import numpy as np
 import pytest
 import torch
@@ -58,9 +58,9 @@ def sample_rows(N, G, shift, boundary, L, cls):
         slots = set(range(min(R, n))) | set(range(max(0, n - R), n))
         # around the wrap point and the valid-length boundary
         for j in range(n):
-            if (j > 0 and seg[j] < seg[j - 1]) or (seg[j] == L):
+            if (j > 0 and seg[j] != seg[j - 1] + 1) or (seg[j] == L):
                 slots |= set(range(max(0, j - R // 2), min(n, j + R // 2)))
-        if s and cls == 1 and boundary == syn.WRAP and g == len(segs) - 1:
+        if s and cls == 1 and boundary != syn.SPLIT and g == len(segs) - 1:
             slots |= set(range(max(0, s - R // 2), min(n, s + R // 2)))
         rows = seg[sorted(slots)]
         tail = seg[max(0, n - R):]
@@ -143,7 +143,12 @@ def test_ratio_sweep_split(G):
                    128, G, syn.SPLIT, 12288, True)
 
 
-@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT])
+def test_headline_shape_cyclic_32k():
+    # the cyclic-causal boundary variant at the headline shape
+    check_workload(3, 2, 1, 32768, 32, 128, 8192, syn.CYCLIC, 32768, True)
+
+
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT, syn.CYCLIC])
 def test_ragged_100k(boundary):
     check_workload(5, boundary, 1, 102400, 32, 128, 25600, boundary, 100000,
                    True)

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 s2a = pytest.importorskip("sparse_attention_long_attn_amd")
 
-BNAME = {syn.WRAP: "wrap", syn.SPLIT: "split"}
+BNAME = {syn.WRAP: "wrap", syn.SPLIT: "split", syn.CYCLIC: "cyclic"}
 
 # B, N, H, D, G, L, half(shift = half*G/2)
 CASES = [
@@ -64,7 +64,7 @@ def run_case(B, N, H, D, G, L, half, boundary, seed, with_bwd):
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
-@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT])
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT, syn.CYCLIC])
 def test_forward_backward_small(case, boundary):
     run_case(*case, boundary=boundary, seed=CASES.index(case),
              with_bwd=True)
@@ -76,7 +76,7 @@ MAP_CASES = [(8, 4), (16, 4), (64, 16), (48, 12), (12, 12), (24, 2),
 
 
 @pytest.mark.parametrize("N,G", MAP_CASES)
-@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT])
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT, syn.CYCLIC])
 @pytest.mark.parametrize("half", [0, 1])
 def test_group_map_bit_exact(N, G, boundary, half):
     shift = half * G // 2

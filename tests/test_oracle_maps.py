@@ -12,7 +12,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (WRAP, SPLIT, OracleError, adjacency_block,
+from oracle import (WRAP, SPLIT, CYCLIC, OracleError, adjacency_block,
                     adjacency_dense, allowed_pairs, group_maps_a,
                     group_maps_b, segments, validate)
 
@@ -116,7 +116,7 @@ MAP_CASES = [(8, 4), (16, 4), (64, 16), (48, 12), (12, 12), (24, 2),
 
 
 @pytest.mark.parametrize("N,G", MAP_CASES)
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 @pytest.mark.parametrize("half", [0, 1])
 def test_maps_a_equal_b(N, G, boundary, half):
     shift = half * G // 2
@@ -135,9 +135,11 @@ def _brute_sets(cls, N, G, boundary, L):
     pos = list(range(N))
     if s == 0:
         chunks = [pos[t:t + G] for t in range(0, N, G)]
-    elif boundary == WRAP:
+    elif boundary in (WRAP, CYCLIC):
         rolled = pos[s:] + pos[:s]
         chunks = [rolled[t:t + G] for t in range(0, N, G)]
+        if boundary == CYCLIC:       # causal order = original order
+            chunks = [sorted(ch) for ch in chunks]
     else:
         cuts = [0, s] + [s + t * G for t in range(1, N // G)] + [N]
         chunks = [pos[a:b] for a, b in zip(cuts[:-1], cuts[1:])]
@@ -150,7 +152,7 @@ def _brute_sets(cls, N, G, boundary, L):
 
 @pytest.mark.parametrize("N,G", [(8, 4), (16, 4), (24, 6), (12, 12), (20, 4),
                                  (32, 8)])
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 @pytest.mark.parametrize("L", [1, 3, 4, 5, 7, 8, None])
 def test_adjacency_brute_force(N, G, boundary, L):
     """Validation lengths 1,3,4,5,7,8 cover partial groups (PaperTrace
@@ -175,6 +177,8 @@ def test_pair_counts_closed_form(N, G):
     split1 = (M - 1) * per_group + s * (s + 1) if s else c0
     assert allowed_pairs(N, G, G // 2, WRAP, N) == (c0, wrap1)
     assert allowed_pairs(N, G, G // 2, SPLIT, N) == (c0, split1)
+    # the cyclic-causal graph keeps WRAP's partition, so its triangles too
+    assert allowed_pairs(N, G, G // 2, CYCLIC, N) == (c0, wrap1)
     if M > 1:
         # WRAP adds exactly s*s edges: queries 0..s-1 reading keys N-s..N-1
         assert wrap1 - split1 == s * s
@@ -212,18 +216,30 @@ def test_adjacency_invariants(N, G, L):
     valid = np.arange(N) < L
     extra &= valid[:, None] & valid[None, :]
     assert np.array_equal(w & ~sp, extra)
+    # cyclic-causal: no edge points to a later position; its s*s extra
+    # edges over SPLIT are the tail N-s..N-1 reading the head 0..s-1, the
+    # transpose of WRAP's, so the two modes share exactly SPLIT's edges
+    cy = adjacency_dense(1, N, G, s, CYCLIC, L)
+    tril = np.tril(np.ones((N, N), bool))
+    assert not (cy & ~tril).any()
+    assert not (sp & ~cy).any()
+    back = np.zeros((N, N), bool)
+    back[N - s:, :s] = True
+    back &= valid[:, None] & valid[None, :]
+    assert np.array_equal(cy & ~sp, back)
+    assert np.array_equal(cy & w, sp)
 
 
 def test_g_equals_n_is_full_causal():
     for N in (4, 8, 12, 16):
-        for boundary in (WRAP, SPLIT):
+        for boundary in (WRAP, SPLIT, CYCLIC):
             for cls in (0, 1):
                 a = adjacency_dense(cls, N, N, N // 2, boundary, N)
                 assert np.array_equal(a, np.tril(np.ones((N, N), bool)))
 
 
 def test_shift_zero_both_classes_equal():
-    for boundary in (WRAP, SPLIT):
+    for boundary in (WRAP, SPLIT, CYCLIC):
         a0 = adjacency_dense(0, 64, 16, 0, boundary, 64)
         a1 = adjacency_dense(1, 64, 16, 0, boundary, 64)
         assert np.array_equal(a0, a1)
@@ -236,7 +252,7 @@ def test_shift_zero_both_classes_equal():
     dict(N=64, H=4, D=16, G=15, shift=7, boundary=WRAP, L=60),
     dict(N=60, H=4, D=16, G=16, shift=8, boundary=WRAP, L=60),
     dict(N=64, H=4, D=16, G=16, shift=4, boundary=WRAP, L=64),
-    dict(N=64, H=4, D=16, G=16, shift=8, boundary=2, L=64),
+    dict(N=64, H=4, D=16, G=16, shift=8, boundary=3, L=64),
     dict(N=64, H=4, D=16, G=16, shift=8, boundary=WRAP, L=0),
     dict(N=64, H=4, D=16, G=16, shift=8, boundary=WRAP, L=65),
 ])

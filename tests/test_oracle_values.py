@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (WRAP, SPLIT, adjacency_block, backward,
+from oracle import (WRAP, SPLIT, CYCLIC, adjacency_block, backward,
                     backward_segments, forward, forward_segments,
                     group_maps_a, segments)
 
@@ -32,7 +32,7 @@ CASES = [  # B, N, H, D, G, L
 
 
 @pytest.mark.parametrize("B,N,H,D,G,L", CASES)
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 @pytest.mark.parametrize("half", [0, 1])
 def test_forward_two_derivations(B, N, H, D, G, L, boundary, half):
     q, k, v = (rand((B, N, H, D), s) for s in (1, 2, 3))
@@ -48,7 +48,7 @@ def test_forward_two_derivations(B, N, H, D, G, L, boundary, half):
 
 
 @pytest.mark.parametrize("B,N,H,D,G,L", CASES)
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_backward_two_derivations(B, N, H, D, G, L, boundary):
     q, k, v, do = (rand((B, N, H, D), s) for s in (4, 5, 6, 7))
     do[:, L:] = 0
@@ -61,7 +61,7 @@ def test_backward_two_derivations(B, N, H, D, G, L, boundary):
         assert np.all(x[:, L:] == 0)
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_unpadded_segments_match_library_sdpa(boundary):
     B, N, H, D, G = 1, 64, 4, 16, 16
     q, k, v = (rand((B, N, H, D), s) for s in (11, 12, 13))
@@ -93,7 +93,7 @@ def _textbook_causal(q, k, v, sc):
 
 
 @pytest.mark.parametrize("N", [4, 8, 12, 16])
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_g_equals_n_brute_force(N, boundary):
     B, H, D = 1, 2, 3
     q, k, v = (rand((B, N, H, D), s) for s in (21, 22, 23))
@@ -105,7 +105,7 @@ def test_g_equals_n_brute_force(N, boundary):
         assert np.max(np.abs(lse[0, h] - rl)) <= 1e-12
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_slot0_rows_exact(boundary):
     """The first member of every group sees only itself: o = v exactly and
     lse = z_ii."""
@@ -122,7 +122,7 @@ def test_slot0_rows_exact(boundary):
             assert abs(lse[0, h, x] - sc * (q[0, x, h] @ k[0, x, h])) <= 1e-13
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_padding_invariance(boundary):
     """Changing padded rows of q, k, v leaves valid outputs bit-identical
     (padding never enters a softmax)."""
@@ -142,7 +142,7 @@ def test_padding_invariance(boundary):
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_leak_perturb_key(boundary):
     """Editing k/v at position t changes exactly the rows whose visible set
     holds t.  Under SPLIT no row before t changes; under WRAP the rows < s
@@ -186,7 +186,7 @@ def test_lse_bounds_and_reconstruction():
                 assert np.max(np.abs(rec - o[0, i, h])) <= 1e-12
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 @pytest.mark.parametrize("N,G,L", [(8, 4, 8), (8, 4, 5), (16, 4, 13), (12, 12, 12)])
 def test_backward_finite_differences(boundary, N, G, L):
     B, H, D = 1, 2, 3
@@ -213,7 +213,7 @@ def test_backward_finite_differences(boundary, N, G, L):
         assert err < 1e-7, (name, err)
 
 
-@pytest.mark.parametrize("boundary", [WRAP, SPLIT])
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
 def test_backward_invariants(boundary):
     B, N, H, D, G, L = 1, 64, 4, 8, 16, 57
     q, k, v, do = (rand((B, N, H, D), s) for s in (81, 82, 83, 84))
