@@ -176,8 +176,18 @@ def _heads_rows(H, N, heads, rows):
     return heads, rows
 
 
+def _with_docs(am, doc, b, rb, cols):
+    """Document mask: a query only reads keys of its own document, in both
+    head classes ([LL] §1.1, paragraph on causal masks and sample packing:
+    the same document-ID constraint for the original and the shifted
+    partition).  doc: integer [B, N] or None."""
+    if doc is None:
+        return am
+    return am & (doc[b, rb][:, None] == doc[b, cols][None, :])
+
+
 def forward(q, k, v, G, shift, boundary, L, scale, heads=None, rows=None,
-            block=256):
+            block=256, doc=None):
     """Dense masked softmax attention over the derivation-A edge sets.
 
     For each valid query i with visible set S_i:
@@ -188,6 +198,7 @@ def forward(q, k, v, G, shift, boundary, L, scale, heads=None, rows=None,
 
     q, k, v: float64 [B, N, H, D].  Returns o [B,N,H,D] and lse [B,H,N];
     rows >= L (and rows / heads not requested) hold o = 0, lse = -inf.
+    doc: optional integer [B, N] document IDs (see _with_docs).
     Only the columns some row of a block can see are gathered: masked terms
     are exact zeros, so this changes no value."""
     B, N, H, D = q.shape
@@ -204,8 +215,8 @@ def forward(q, k, v, G, shift, boundary, L, scale, heads=None, rows=None,
             live = a.any(axis=1)
             if cols.size == 0:
                 continue
-            am = a[:, cols]
             for b in range(B):
+                am = _with_docs(a[:, cols], doc, b, rb, cols)
                 z = (q[b, rb, h] @ k[b, cols, h].T) * scale
                 z = np.where(am, z, -np.inf)
                 m = np.where(live, z.max(axis=1, initial=-np.inf), 0.0)
@@ -219,7 +230,7 @@ def forward(q, k, v, G, shift, boundary, L, scale, heads=None, rows=None,
 
 
 def backward(q, k, v, do, G, shift, boundary, L, scale, heads=None,
-             rows=None, block=256):
+             rows=None, block=256, doc=None):
     """Gradients of sum(dO * O) with respect to q, k, v, evaluated from the
     definition.  With a_ij = exp(z_ij - lse_i) and g = dO_i, the gradient
     with respect to a logit is dL/dz_ij = a_ij * g.(v_j - o_i)
@@ -248,8 +259,8 @@ def backward(q, k, v, do, G, shift, boundary, L, scale, heads=None,
             live = a_.any(axis=1)
             if cols.size == 0:
                 continue
-            am = a_[:, cols]
             for b in range(B):
+                am = _with_docs(a_[:, cols], doc, b, rb, cols)
                 z = (q[b, rb, h] @ k[b, cols, h].T) * scale
                 z = np.where(am, z, -np.inf)
                 m = np.where(live, z.max(axis=1, initial=-np.inf), 0.0)
@@ -315,10 +326,12 @@ def group_maps_b(N: int, G: int, shift: int, boundary: int):
     return gid, slot, src
 
 
-def _segment_softmax(qs, ks, pos, L, scale):
+def _segment_softmax(qs, ks, pos, L, scale, dseg=None):
     n = len(pos)
     live = pos < L
     allow = np.tril(np.ones((n, n), bool)) & live[None, :] & live[:, None]
+    if dseg is not None:
+        allow &= dseg[:, None] == dseg[None, :]
     s = (qs @ ks.T) * scale
     s = np.where(allow, s, -np.inf)
     mx = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
@@ -329,7 +342,7 @@ def _segment_softmax(qs, ks, pos, L, scale):
     return p, lse, live
 
 
-def forward_segments(q, k, v, G, shift, boundary, L, scale):
+def forward_segments(q, k, v, G, shift, boundary, L, scale, doc=None):
     """Derivation B of the forward: for every head and group, gather the
     group's rows in group order, run ordinary causal softmax attention on
     that short sequence (keys at positions >= L masked), and scatter the
@@ -342,14 +355,15 @@ def forward_segments(q, k, v, G, shift, boundary, L, scale):
     for b in range(B):
         for h in range(H):
             for pos in segs[head_class(h, H)]:
-                p, ls, live = _segment_softmax(q[b, pos, h], k[b, pos, h],
-                                               pos, L, scale)
+                p, ls, live = _segment_softmax(
+                    q[b, pos, h], k[b, pos, h], pos, L, scale,
+                    None if doc is None else doc[b, pos])
                 o[b, pos, h] = np.where(live[:, None], p @ v[b, pos, h], 0.0)
                 lse[b, h, pos] = ls
     return o, lse
 
 
-def backward_segments(q, k, v, do, G, shift, boundary, L, scale):
+def backward_segments(q, k, v, do, G, shift, boundary, L, scale, doc=None):
     """Derivation B of the backward: per group, the textbook softmax
     backward dS = P * (dP - rowsum(P * dP)) with dP = dO V^T, then
     dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, scattered back."""
@@ -363,7 +377,8 @@ def backward_segments(q, k, v, do, G, shift, boundary, L, scale):
         for h in range(H):
             for pos in segs[head_class(h, H)]:
                 qs, ks, vs = q[b, pos, h], k[b, pos, h], v[b, pos, h]
-                p, _, live = _segment_softmax(qs, ks, pos, L, scale)
+                p, _, live = _segment_softmax(
+                    qs, ks, pos, L, scale, None if doc is None else doc[b, pos])
                 g = np.where(live[:, None], do[b, pos, h], 0.0)
                 dp = g @ vs.T
                 ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))

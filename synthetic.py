@@ -97,5 +97,27 @@ def make_inputs(config: int, variant: int, B: int, N: int, H: int, D: int,
     return out
 
 
+def make_doc_ids(seed: int, B: int, N: int, mean_len: int,
+                 cuts=()) -> np.ndarray:
+    """Packed-sequence document IDs, int32 [B, N], non-decreasing along each
+    row: document lengths are drawn from a geometric distribution with the
+    given mean (a mix of short and long samples), and every position in
+    ``cuts`` additionally starts a new document (to place boundaries inside
+    a group, on an original group boundary or on a shifted one)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((B, N), np.int32)
+    for b in range(B):
+        starts = np.zeros(N, bool)
+        x = 0
+        while x < N:
+            starts[x] = True
+            x += int(g.geometric(1.0 / max(1, mean_len)))
+        for c in cuts:
+            if 0 <= c < N:
+                starts[c] = True
+        out[b] = np.cumsum(starts) - 1
+    return out
+
+
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import synthetic as syn
 from oracle import (WRAP, SPLIT, CYCLIC, adjacency_block, backward,
                     backward_segments, forward, forward_segments,
                     group_maps_a, segments)
@@ -244,3 +245,74 @@ def test_restricted_rows_match_full():
     part = backward(q, k, v, do, G, G // 2, WRAP, L, sc, heads=[3], rows=rows)
     for t in range(3):
         assert np.max(np.abs(part[t][0, rows, 3] - full[t][0, rows, 3])) <= 1e-12
+
+
+# ------------------------------------------------------------ document mask
+def _docs(B, N, G, seed):
+    # boundaries inside a group, on an original boundary and on a shifted one
+    return syn.make_doc_ids(seed, B, N, mean_len=max(2, G // 2),
+                            cuts=(G // 3, G, G + G // 2))
+
+
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
+@pytest.mark.parametrize("L", [48, 41])
+def test_documents_two_derivations(boundary, L):
+    B, N, H, D, G = 2, 48, 4, 8, 12
+    q, k, v, do = (rand((B, N, H, D), s) for s in (91, 92, 93, 94))
+    doc = _docs(B, N, G, 95)
+    sc = 1 / math.sqrt(D)
+    oa, la = forward(q, k, v, G, G // 2, boundary, L, sc, doc=doc)
+    ob, lb = forward_segments(q, k, v, G, G // 2, boundary, L, sc, doc=doc)
+    assert np.max(np.abs(oa - ob)) <= 1e-12
+    fa, fb = np.isfinite(la), np.isfinite(lb)
+    assert np.array_equal(fa, fb) and np.max(np.abs(la[fa] - lb[fb])) <= 1e-12
+    ga = backward(q, k, v, do, G, G // 2, boundary, L, sc, doc=doc)[:3]
+    gb = backward_segments(q, k, v, do, G, G // 2, boundary, L, sc, doc=doc)
+    for x, y in zip(ga, gb):
+        assert np.max(np.abs(x - y)) <= 1e-12
+
+
+@pytest.mark.parametrize("boundary", [WRAP, SPLIT, CYCLIC])
+def test_documents_leak(boundary):
+    # [LL] §1.1: changing an earlier document must leave a later document's
+    # outputs unchanged (boundaries inside a group and on both partitions'
+    # boundaries)
+    B, N, H, D, G, L = 1, 64, 4, 8, 16, 64
+    q, k, v, do = (rand((B, N, H, D), s) for s in (101, 102, 103, 104))
+    doc = _docs(B, N, G, 105)
+    sc = 1 / math.sqrt(D)
+    first = doc[0] == doc[0, 0]
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for t in (q2, k2, v2):
+        t[:, first] += rand(t[:, first].shape, 106)
+    r1 = backward(q, k, v, do, G, G // 2, boundary, L, sc, doc=doc)
+    r2 = backward(q2, k2, v2, do, G, G // 2, boundary, L, sc, doc=doc)
+    later = ~first
+    for x, y in zip(r1, r2):
+        if x.ndim == 4:
+            assert np.array_equal(x[:, later], y[:, later])
+        else:
+            assert np.array_equal(x[..., later], y[..., later])
+
+
+def test_documents_special_cases():
+    B, N, H, D, G, L = 1, 32, 2, 8, 8, 32
+    q, k, v, do = (rand((B, N, H, D), s) for s in (111, 112, 113, 114))
+    sc = 1 / math.sqrt(D)
+    for boundary in (WRAP, SPLIT, CYCLIC):
+        # one document: identical to no document mask
+        one = np.zeros((B, N), np.int32)
+        a = backward(q, k, v, do, G, G // 2, boundary, L, sc)
+        b = backward(q, k, v, do, G, G // 2, boundary, L, sc, doc=one)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+        # one token per document: o = v, lse = scale q.k, no q/k gradient
+        own = np.arange(N, dtype=np.int32)[None, :]
+        dq, dk, dv, o, lse = backward(q, k, v, do, G, G // 2, boundary, L,
+                                      sc, doc=own)
+        assert np.max(np.abs(o - v)) <= 1e-15
+        qk = np.einsum("bnhd,bnhd->bhn", q, k) * sc
+        assert np.max(np.abs(lse - qk)) <= 1e-14
+        # (zero up to the summation order of g.v against g.o)
+        assert np.max(np.abs(dq)) <= 1e-14 and np.max(np.abs(dk)) <= 1e-14
+        assert np.max(np.abs(dv - do)) <= 1e-15
