@@ -67,7 +67,7 @@ typedef enum { S2A_BF16 = 0, S2A_F32 = 1 } s2a_dtype;
 /*
  * Forward.  For every head h, group and query x < valid_len with visible
  * set S_x (same group, at or before x in group order, key position <
- * valid_len):
+ * valid_len, and -- if doc_ids is given -- the same document as x):
  *   o[x]   = sum_{y in S_x} softmax_y(scale * q[x].k[y]) v[y]
  *   lse[x] = ln sum_{y in S_x} exp(scale * q[x].k[y])
  * (PaperTrace LongLoRA §3, the equation for o_i^s; the per-row
@@ -77,14 +77,20 @@ typedef enum { S2A_BF16 = 0, S2A_F32 = 1 } s2a_dtype;
  * Arguments: q, k, v bf16 [B,N,H,D]; o of dtype o_dtype [B,N,H,D];
  * lse f32 [B,H,N]; N the padded length; shift 0 (plain grouping) or G/2;
  * valid_len in [1, N]; scale > 0 and finite (1/sqrt(D) in the method).
+ * doc_ids: NULL, or int32 [B, N] document IDs of a packed sequence (any
+ * values; two positions are in one document iff their IDs are equal): a
+ * query then reads only keys of its own document, with the same rule for
+ * both head classes (PaperTrace LongLoRA §1.1, paragraph on causal masks
+ * and sample packing).  Every valid query still sees itself.
  * Checks (PaperTrace LongLoRA §1, launch-time asserts): H % 2 == 0,
- * G % 2 == 0, N % G == 0, all sizes > 0, pointers non-NULL and 16-byte
- * aligned.  Returns S2A_EINVAL / S2A_EUNSUPPORTED / S2A_EHIP / S2A_OK.
+ * G % 2 == 0, N % G == 0, all sizes > 0, tensor pointers non-NULL and
+ * 16-byte aligned, doc_ids 4-byte aligned.  Returns S2A_EINVAL /
+ * S2A_EUNSUPPORTED / S2A_EHIP / S2A_OK.
  */
 s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
                       int o_dtype, float *lse, int B, int N, int H, int D,
                       int G, int shift, int boundary, int valid_len,
-                      float scale, void *stream);
+                      const int *doc_ids, float scale, void *stream);
 
 /*
  * Backward.  Given dout = dL/do and the o, lse produced by s2attn_fwd with
@@ -98,15 +104,16 @@ s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
  * of dq, dk and dv are exactly 0.
  *
  * delta_ws: caller-provided f32 workspace of B*H*N floats; on return it
- * holds delta_x.  Every output element is written exactly once (no
- * atomics), so results are bitwise repeatable.
+ * holds delta_x.  doc_ids: as for s2attn_fwd (the same array).  Every
+ * output element is written exactly once (no atomics), so results are
+ * bitwise repeatable.
  */
 s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       const void *o, int o_dtype, const float *lse,
                       const void *dout, float *dq, float *dk, float *dv,
                       float *delta_ws, int B, int N, int H, int D, int G,
-                      int shift, int boundary, int valid_len, float scale,
-                      void *stream);
+                      int shift, int boundary, int valid_len,
+                      const int *doc_ids, float scale, void *stream);
 
 /*
  * The three stages of s2attn_bwd, for callers that schedule or time them
@@ -126,14 +133,15 @@ s2a_status s2attn_bwd_dkdv(const void *q, const void *k, const void *v,
                            const float *lse, const float *delta_ws,
                            const void *dout, float *dk, float *dv, int B,
                            int N, int H, int D, int G, int shift,
-                           int boundary, int valid_len, float scale,
-                           void *stream);
+                           int boundary, int valid_len, const int *doc_ids,
+                           float scale, void *stream);
 
 s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
                          const float *lse, const float *delta_ws,
                          const void *dout, float *dq, int B, int N, int H,
                          int D, int G, int shift, int boundary,
-                         int valid_len, float scale, void *stream);
+                         int valid_len, const int *doc_ids, float scale,
+                         void *stream);
 
 /*
  * Group index maps, computed on the device by the same group geometry the

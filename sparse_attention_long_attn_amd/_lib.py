@@ -38,18 +38,20 @@ def load() -> ctypes.CDLL:
             "fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.s2attn_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, F, P]
+    # ... boundary, valid_len, doc_ids, scale, stream
+    lib.s2attn_fwd.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, P, F,
+                               P]
     lib.s2attn_fwd.restype = I
     lib.s2attn_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
-                               I, I, I, I, I, I, I, I, F, P]
+                               I, I, I, I, I, I, I, I, P, F, P]
     lib.s2attn_bwd.restype = I
     lib.s2attn_bwd_preprocess.argtypes = [P, I, P, P, I, I, I, I, P]
     lib.s2attn_bwd_preprocess.restype = I
     lib.s2attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P,
-                                    I, I, I, I, I, I, I, I, F, P]
+                                    I, I, I, I, I, I, I, I, P, F, P]
     lib.s2attn_bwd_dkdv.restype = I
     lib.s2attn_bwd_dq.argtypes = [P, P, P, P, P, P, P,
-                                  I, I, I, I, I, I, I, I, F, P]
+                                  I, I, I, I, I, I, I, I, P, F, P]
     lib.s2attn_bwd_dq.restype = I
     lib.s2attn_group_map.argtypes = [I, I, I, I, I, P, P, P, P]
     lib.s2attn_group_map.restype = I

@@ -20,6 +20,7 @@ s2a_status fail(s2a_status st, const char *fmt, long long a = 0,
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Launch-time checks of the group shape: H % 2 == 0, G % 2 == 0 and
 // N % G == 0 after padding, the valid length inside [1, N], and only the
@@ -64,8 +65,9 @@ S2AGeom make_geom(int N, int G, int shift, int boundary, int L) {
 }
 
 S2AParams make_params(int B, int N, int H, int G, int shift, int boundary,
-                      int L, float scale, int tile_rows) {
+                      int L, float scale, int tile_rows, const int *doc) {
   S2AParams p;
+  p.doc = doc;
   p.g = make_geom(N, G, shift, boundary, L);
   p.B = B;
   p.H = H;
@@ -109,10 +111,12 @@ extern "C" {
 s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
                       int o_dtype, float *lse, int B, int N, int H, int D,
                       int G, int shift, int boundary, int valid_len,
-                      float scale, void *stream) {
+                      const int *doc_ids, float scale, void *stream) {
   g_err[0] = 0;
   s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
   if (st != S2A_OK) return st;
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
   if (!q || !k || !v || !o || !lse)
     return fail(S2A_EINVAL, "NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -123,7 +127,7 @@ s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, s2a_fwd_tile_rows(D));
+                                  scale, s2a_fwd_tile_rows(D), doc_ids);
   return hip_status(s2a_launch_fwd(q, k, v, o, o_dtype == S2A_F32, lse, D, p,
                                    (hipStream_t)stream),
                     "forward launch");
@@ -133,11 +137,13 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       const void *o, int o_dtype, const float *lse,
                       const void *dout, float *dq, float *dk, float *dv,
                       float *delta_ws, int B, int N, int H, int D, int G,
-                      int shift, int boundary, int valid_len, float scale,
-                      void *stream) {
+                      int shift, int boundary, int valid_len,
+                      const int *doc_ids, float scale, void *stream) {
   g_err[0] = 0;
   s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
   if (st != S2A_OK) return st;
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws)
     return fail(S2A_EINVAL, "NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -149,7 +155,7 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, 1);
+                                  scale, 1, doc_ids);
   return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
                                    dq, dk, dv, delta_ws, D, p,
                                    (hipStream_t)stream),
@@ -178,14 +184,16 @@ s2a_status s2attn_bwd_dkdv(const void *q, const void *k, const void *v,
                            const float *lse, const float *delta_ws,
                            const void *dout, float *dk, float *dv, int B,
                            int N, int H, int D, int G, int shift,
-                           int boundary, int valid_len, float scale,
-                           void *stream) {
+                           int boundary, int valid_len, const int *doc_ids,
+                           float scale, void *stream) {
   g_err[0] = 0;
   s2a_status st = check_grad_stage(q, k, v, lse, delta_ws, dout, dk, dv, B, N,
                                    H, D, G, shift, boundary, valid_len, scale);
   if (st != S2A_OK) return st;
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, 1);
+                                  scale, 1, doc_ids);
   return hip_status(s2a_launch_bwd_dkdv(q, k, v, dout, lse, delta_ws, dk, dv,
                                         D, p, (hipStream_t)stream),
                     "dK/dV launch");
@@ -195,13 +203,16 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
                          const float *lse, const float *delta_ws,
                          const void *dout, float *dq, int B, int N, int H,
                          int D, int G, int shift, int boundary,
-                         int valid_len, float scale, void *stream) {
+                         int valid_len, const int *doc_ids, float scale,
+                         void *stream) {
   g_err[0] = 0;
   s2a_status st = check_grad_stage(q, k, v, lse, delta_ws, dout, dq, dq, B, N,
                                    H, D, G, shift, boundary, valid_len, scale);
   if (st != S2A_OK) return st;
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
-                                  scale, 1);
+                                  scale, 1, doc_ids);
   return hip_status(s2a_launch_bwd_dq(q, k, v, dout, lse, delta_ws, dq, D, p,
                                       (hipStream_t)stream),
                     "dQ launch");

@@ -18,7 +18,13 @@
 //                        forward's orientation (one query per lane column):
 //                          S^T = K Q^T, dP^T = V dO^T, dS^T as above,
 //                          dQ^T += K^T dS^T
-//                        and stores dQ once at the end.
+//                        and stores dQ once at the end;
+//   s2a_bwd_dkdv_lo_kernel (D >= 64) adds the bf16 rounding residuals of P
+//                        and dS of "hot" query tiles (queries that see few
+//                        keys) to dK and dV.
+// Under a document mask (packed sequences) a pair also needs equal document
+// IDs, in both head classes (PaperTrace 4.1.2, §1.1, the paragraph on
+// causal masks and sample packing).
 // Splitting dQ off costs 4*D extra MFMA work per pair (S and dP are
 // recomputed) but replaces fp32 atomics whose traffic (one read-modify-
 // write of a 64x128 fp32 tile per key tile and query tile) cost more than
@@ -38,6 +44,12 @@ constexpr int DQ_BK = 64;    // keys per inner tile of the dQ kernel
 constexpr int THREADS = 256;      // dK/dV workgroup
 constexpr int DQ_THREADS = DQ_BQ / 32 * 64;
 constexpr int DQ_MINBLOCKS = 512 / DQ_THREADS;  // two waves per SIMD
+// A query is "hot" when it sees few keys: it lies in the first HOT_SPAN
+// slots of its group or, under a document mask, fewer than HOT_SPAN slots
+// after the start of its document.  Its softmax weights and dS entries are
+// then large and their bf16 rounding is not averaged away, so products
+// that involve hot queries take P and dS as bf16 hi + lo parts.
+constexpr int HOT_SPAN = 64;
 
 template <int D>
 struct BwdDims {
@@ -124,7 +136,7 @@ __device__ __forceinline__ UnitTile decode(const S2AParams &p, bool reverse) {
 // ---------------------------------------------------------------------------
 // dK, dV (key-outer)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool DOC>
 __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -139,6 +151,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t dOs[2 * QT];
   __shared__ __attribute__((aligned(16))) float lse2s[2 * KV_BQ];
   __shared__ __attribute__((aligned(16))) float dlts[2 * KV_BQ];
+  __shared__ __attribute__((aligned(16))) int qdocs[2 * KV_BQ];  // DOC only
+  __shared__ __attribute__((aligned(16))) int hotrow[2 * KV_BQ];  // DOC only
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -165,6 +179,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
   const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
   const bool wave_keys_valid = __all(kvalid);
+  const int kdoc = DOC ? p.doc[(size_t)ut.b * N + kpos] : 0;
 
   bf16x8 kreg[Dm::KSTEPS], vreg[Dm::KSTEPS];
   {
@@ -185,6 +200,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
   // get q = dO = 0, lse = +inf (so P = 0) and delta = 0 (so dS = 0).
   u32x4 qst[NCH], gst[NCH];
   float l2st = INFINITY, dlst = 0.f;
+  // DOC: document IDs of query q0 + tid and of the slot HOT_SPAN before it
+  int qdst = 0, qref = 0;
+  bool qhin = false;
   auto fetch = [&](int q0) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -207,6 +225,12 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       const int qsl = q0 + tid;
       l2st = INFINITY;
       dlst = 0.f;
+      if (DOC) {
+        const int *db = p.doc + (size_t)ut.b * N;
+        qhin = qsl < glen;
+        qdst = db[qhin ? run.pos(qsl) : 0];
+        qref = db[qhin ? run.pos(qsl >= HOT_SPAN ? qsl - HOT_SPAN : 0) : 0];
+      }
       if (qsl < glen) {
         const int qp = run.pos(qsl);
         if (qp < L) {
@@ -227,6 +251,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
     if (tid < KV_BQ) {
       lse2s[buf * KV_BQ + tid] = l2st;
       dlts[buf * KV_BQ + tid] = dlst;
+      if (DOC) {
+        qdocs[buf * KV_BQ + tid] = qdst;
+        hotrow[buf * KV_BQ + tid] = qhin && qref != qdst;
+      }
     }
   };
 
@@ -250,6 +278,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
     const bool more = it + 1 < nq;
     if (more) fetch(q0 + KV_BQ);  // in flight during this tile's math
 
+    static_assert(KV_BQ == 64, "one hot flag per lane");
+    const bool hot = q0 < HOT_SPAN || (DOC && __any(hotrow[buf * KV_BQ + lane] != 0));
     if (q0 + KV_BQ - 1 >= kw0) {  // else all queries precede the wave's keys
       const bf16_t *Qb = Qs + buf * QT;
       const bf16_t *dOb = dOs + buf * QT;
@@ -273,7 +303,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
         }
       }
       // P and dS.  Element i of block qb is query q0 + 32qb + 8(i/4) + 4hf + i%4.
-      const bool edge = (q0 < kw0 + 31) || !wave_keys_valid;
+      const bool edge = DOC || (q0 < kw0 + 31) || !wave_keys_valid;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -281,11 +311,15 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
           const int r0 = 32 * qb + 8 * i4 + 4 * hf;
           const f32x4 l2 = *(const f32x4 *)(l2b + r0);
           const f32x4 dl = *(const f32x4 *)(dlb + r0);
+          i32x4 qd = {0, 0, 0, 0};
+          if (DOC) qd = *(const i32x4 *)(qdocs + buf * KV_BQ + r0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
             float pp = __builtin_amdgcn_exp2f(fmaf(sacc[qb][i], c2, -l2[e]));
-            if (edge && !(kvalid && key <= q0 + r0 + e)) pp = 0.f;
+            bool ok = kvalid & (key <= q0 + r0 + e);
+            if (DOC) ok &= qd[e] == kdoc;
+            if (edge) pp = ok ? pp : 0.f;
             dpacc[qb][i] = pp * (dpacc[qb][i] - dl[e]);
             sacc[qb][i] = pp;
           }
@@ -300,6 +334,17 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
                                     sp[e0 + 4], sp[e0 + 5], sp[e0 + 6], sp[e0 + 7]);
         const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
                                     dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+        bf16x8 pl = pb, sl = sb;  // rounding residuals (hot tiles)
+        if (hot) {
+          pl = to_bf16x8(sp[e0] - (float)pb[0], sp[e0 + 1] - (float)pb[1],
+                         sp[e0 + 2] - (float)pb[2], sp[e0 + 3] - (float)pb[3],
+                         sp[e0 + 4] - (float)pb[4], sp[e0 + 5] - (float)pb[5],
+                         sp[e0 + 6] - (float)pb[6], sp[e0 + 7] - (float)pb[7]);
+          sl = to_bf16x8(dp[e0] - (float)sb[0], dp[e0 + 1] - (float)sb[1],
+                         dp[e0 + 2] - (float)sb[2], dp[e0 + 3] - (float)sb[3],
+                         dp[e0 + 4] - (float)sb[4], dp[e0 + 5] - (float)sb[5],
+                         dp[e0 + 6] - (float)sb[6], dp[e0 + 7] - (float)sb[7]);
+        }
         const int ro = (16 * qs + trow) * KP + tcol;
 #pragma unroll
         for (int db = 0; db < Dm::DB; ++db) {
@@ -309,6 +354,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
           const bf16x8 aq = cat4(lds_read_tr(Qb + ro + 32 * db),
                                  lds_read_tr(Qb + ro + 8 * KP + 32 * db));
           dkacc[db] = mfma32(aq, sb, dkacc[db]);
+          if (hot) {
+            dvacc[db] = mfma32(ag, pl, dvacc[db]);
+            dkacc[db] = mfma32(aq, sl, dkacc[db]);
+          }
         }
       }
     }
@@ -339,7 +388,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // dQ (query-outer)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool DOC>
 __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -352,6 +401,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
   constexpr int NCH = (TCH + DQ_THREADS - 1) / DQ_THREADS;    // chunks per thread
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
+  __shared__ __attribute__((aligned(16))) int kdoc[2][DQ_BK];  // DOC only
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -378,6 +428,12 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
+  const int qdoc = DOC ? p.doc[(size_t)ut.b * N + qpos] : 0;
+  // a hot query (see HOT_SPAN) reads keys of at most two key tiles: the
+  // diagonal one and the one before it
+  const bool wave_hot =
+      DOC && __any(qin && p.doc[(size_t)ut.b * N +
+                                run.pos(qslot >= HOT_SPAN ? qslot - HOT_SPAN : 0)] != qdoc);
 
   bf16x8 qreg[Dm::KSTEPS], greg[Dm::KSTEPS];
   {
@@ -395,7 +451,12 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
   }
 
   u32x4 kst[NCH], vst[NCH];
+  int kdst = 0;  // document ID of key k0 + tid (DOC, tid < DQ_BK)
   auto fetch = [&](int k0) {
+    if (DOC && tid < DQ_BK) {
+      const int ks = k0 + tid;
+      kdst = p.doc[(size_t)ut.b * N + (ks < glen ? run.pos(ks) : 0)];
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * DQ_THREADS;
@@ -415,6 +476,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
     }
   };
   auto stage = [&](int buf) {
+    if (DOC && tid < DQ_BK) kdoc[buf][tid] = kdst;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * DQ_THREADS;
@@ -468,35 +530,55 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
       }
       // dS^T; element i of block kb is key k0 + 32kb + 8(i/4) + 4hf + i%4.
       const int kstop = min(k0 + DQ_BK, glen);
-      const bool edge = (k0 + DQ_BK - 1 > wq_lo) || (k0 + DQ_BK > glen) ||
+      const bool diag = (k0 + DQ_BK - 1 > wq_lo) || (k0 + DQ_BK > glen) ||
                         s2a_range_has_padding(run, k0, kstop, N, L);
+      const bool edge = DOC || diag;
+      const bool resid = diag || (wave_hot && k0 + 2 * DQ_BK - 2 >= wq_lo);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
-          if (edge) {
-            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!(ks <= qslot && ks < glen && run.pos(ks) < L))
-              pp = 0.f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          i32x4 kd = {0, 0, 0, 0};
+          if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * g4 + j;
+            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
+            if (edge) {
+              const int ks = k0 + 32 * kb + 8 * g4 + 4 * hf + j;
+              bool ok = (ks <= qslot) & (ks < glen) & (run.pos(ks) < L);
+              if (DOC) ok &= kd[j] == qdoc;
+              pp = ok ? pp : 0.f;
+            }
+            dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
           }
-          dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
         }
-      // dQ^T += K^T dS^T, 16 keys per MFMA (same key order on both sides).
+      // dQ^T += K^T dS^T, 16 keys per MFMA (same key order on both sides);
+      // on the tiles where rows see few keys, dS goes in as bf16 hi + lo.
+      auto dq_product = [&](auto lo_tag) {
+        constexpr bool LO = decltype(lo_tag)::value;
 #pragma unroll
-      for (int ks = 0; ks < DQ_BK / 16; ++ks) {
-        const f32x16 &dp = dpacc[ks >> 1];
-        const int e0 = 8 * (ks & 1);
-        const bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
-                                    dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
-        const bf16_t *kr = Kb + (16 * ks + trow) * KP + tcol;
+        for (int ks = 0; ks < DQ_BK / 16; ++ks) {
+          const f32x16 &dp = dpacc[ks >> 1];
+          const int e0 = 8 * (ks & 1);
+          bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
+                                dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
+          if constexpr (LO)
+            sb = to_bf16x8(dp[e0] - (float)sb[0], dp[e0 + 1] - (float)sb[1],
+                           dp[e0 + 2] - (float)sb[2], dp[e0 + 3] - (float)sb[3],
+                           dp[e0 + 4] - (float)sb[4], dp[e0 + 5] - (float)sb[5],
+                           dp[e0 + 6] - (float)sb[6], dp[e0 + 7] - (float)sb[7]);
+          const bf16_t *kr = Kb + (16 * ks + trow) * KP + tcol;
 #pragma unroll
-        for (int db = 0; db < Dm::DB; ++db) {
-          const bf16x8 ak = cat4(lds_read_tr(kr + 32 * db),
-                                 lds_read_tr(kr + 8 * KP + 32 * db));
-          dqacc[db] = mfma32(ak, sb, dqacc[db]);
+          for (int db = 0; db < Dm::DB; ++db) {
+            const bf16x8 ak = cat4(lds_read_tr(kr + 32 * db),
+                                   lds_read_tr(kr + 8 * KP + 32 * db));
+            dqacc[db] = mfma32(ak, sb, dqacc[db]);
+          }
         }
-      }
+      };
+      dq_product(std::false_type{});
+      if (resid) dq_product(std::true_type{});
     }
     if (more) stage(buf ^ 1);
     __syncthreads();
@@ -525,7 +607,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
 
 // dQ for D in {64, 128}: K/V tiles in the swizzled layout of s2a_tile.h,
 // filled by direct global -> LDS loads.
-template <int D>
+template <int D, bool DOC>
 __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -536,6 +618,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = DQ_BK * T::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(16))) int kdoc[2][DQ_BK];  // DOC only
   char *const Ks = smem;
   char *const Vs = smem + 2 * TILEB;
 
@@ -564,6 +647,12 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
+  const int qdoc = DOC ? p.doc[(size_t)ut.b * N + qpos] : 0;
+  // a hot query (see HOT_SPAN) reads keys of at most two key tiles: the
+  // diagonal one and the one before it
+  const bool wave_hot =
+      DOC && __any(qin && p.doc[(size_t)ut.b * N +
+                                run.pos(qslot >= HOT_SPAN ? qslot - HOT_SPAN : 0)] != qdoc);
 
   bf16x8 qreg[KSTEPS], greg[KSTEPS];
   {
@@ -592,6 +681,11 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
     } else {
       ld.general(kbh, rs, run, glen, k0, L, kd);
       ld.general(vbh, rs, run, glen, k0, L, vd);
+    }
+    if (DOC && w == 0) {  // document IDs of the tile's 64 keys
+      const int ks = k0 + lane;
+      g2lds4(p.doc + (size_t)ut.b * N + (ks < glen ? run.pos(ks) : 0),
+             &kdoc[buf][0]);
     }
   };
   // (rows trow and trow + 8 of a 16-row step have different swizzles)
@@ -649,25 +743,35 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
           dpacc[kb] = mfma32(av[t], greg[t], dpacc[kb]);
         }
       }
-      const bool edge = (k0 + DQ_BK - 1 > wq_lo) ||
+      const bool diag = (k0 + DQ_BK - 1 > wq_lo) ||
                         !tile_plain(run, glen, k0, DQ_BK, L);
+      const bool edge = DOC || diag;
+      const bool resid = diag || (wave_hot && k0 + 2 * DQ_BK - 2 >= wq_lo);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
-          if (edge) {
-            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!(ks <= qslot && ks < glen && run.pos(ks) < L))
-              pp = 0.f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          i32x4 kd = {0, 0, 0, 0};
+          if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * g4 + j;
+            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
+            if (edge) {
+              const int ks = k0 + 32 * kb + 8 * g4 + 4 * hf + j;
+              bool ok = (ks <= qslot) & (ks < glen) & (run.pos(ks) < L);
+              if (DOC) ok &= kd[j] == qdoc;
+              pp = ok ? pp : 0.f;
+            }
+            dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
           }
-          dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
         }
-      // dQ^T += K^T dS^T.  On edge tiles (the diagonal, where rows see few
-      // keys and |dS| is largest) dS goes in as bf16 hi + lo parts, which
+      // dQ^T += K^T dS^T.  On diagonal tiles (where rows see few keys and
+      // |dS| is largest), tiles with padding or the group end, and the
+      // tiles of hot queries, dS goes in as bf16 hi + lo parts, which
       // removes most of the bf16 rounding of dS from those rows' error.
-      // pass 0: dS rounded to bf16; pass 1 (edge tiles only): the rounding
-      // residual dS - bf16(dS), also in bf16
+      // pass 0: dS rounded to bf16; pass 1 (those tiles only): the
+      // rounding residual dS - bf16(dS), also in bf16
       auto dq_product = [&](auto lo_tag) {
         constexpr bool LO = decltype(lo_tag)::value;
 #pragma unroll
@@ -691,7 +795,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
         }
       };
       dq_product(std::false_type{});
-      if (edge) dq_product(std::true_type{});
+      if (resid) dq_product(std::true_type{});
     }
     wait_vm_all();
     __syncthreads();
@@ -721,7 +825,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 // The first iterations (the only ones whose queries can precede the
 // workgroup's keys) run a masked copy of the body; the steady state has no
 // mask at all.
-template <int D, int BQ, int NBUF>
+template <int D, int BQ, int NBUF, bool DOC>
 __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -736,6 +840,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * TILEB];
   __shared__ __attribute__((aligned(16))) float lse2s[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) float dlts[NBUF * BQ];
+  __shared__ __attribute__((aligned(16))) int qdocs[NBUF * BQ];  // DOC only
   char *const Qs = smem;
   char *const dOs = smem + NBUF * TILEB;
 
@@ -763,6 +868,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   const bool kin = key < glen;
   const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
+  const int kdoc = DOC ? p.doc[(size_t)ut.b * N + kpos] : 0;
 
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
   {
@@ -785,11 +891,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   // Per-row statistics of a query tile, through registers: rows outside
   // the group or padded get lse = +inf (so P = 0) and delta = 0.
   float l2st = INFINITY, dlst = 0.f;
+  int qdst = 0;  // document ID of query q0 + tid (DOC)
   auto fetch_stats = [&](int q0) {
     if (tid < BQ) {
       const int qsl = q0 + tid;
       l2st = INFINITY;
       dlst = 0.f;
+      if (DOC) qdst = p.doc[(size_t)ut.b * N + (qsl < glen ? run.pos(qsl) : 0)];
       if (qsl < glen) {
         const int qp = run.pos(qsl);
         if (qp < L) {
@@ -803,6 +911,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     if (tid < BQ) {
       lse2s[buf * BQ + tid] = l2st;
       dlts[buf * BQ + tid] = dlst;
+      if (DOC) qdocs[buf * BQ + tid] = qdst;
     }
   };
   auto issue_tile = [&](int q0, int buf) {
@@ -848,6 +957,22 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   wait_vm_all();
   __syncthreads();
 
+  // Bit 16qb + i: element i of 32-query block qb (query
+  // 32qb + 8(i/4) + 4hf + i%4 of the tile in buffer buf) shares this lane's
+  // key document.
+  auto same_doc_mask = [&](int buf) -> unsigned {
+    unsigned m = 0u;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const i32x4 qd = *(const i32x4 *)(qdocs + buf * BQ + 32 * qb + 8 * i4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          m |= (unsigned)(qd[e] == kdoc) << (16 * qb + 4 * i4 + e);
+      }
+    return m;
+  };
   auto body = [&](auto masked_tag, int it) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int q0 = k0 + it * BQ;
@@ -882,6 +1007,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
         l2v[qb][i4] = *(const f32x4 *)(l2b + 32 * qb + 8 * i4 + 4 * hf);
         dlv[qb][i4] = *(const f32x4 *)(dlb + 32 * qb + 8 * i4 + 4 * hf);
       }
+    const unsigned dmask = DOC ? same_doc_mask(buf) : 0u;
     f32x16 S[2], dP[2];
     bf16x8 pb[2][2], sb[2][2];
     // element work of block qb: P = exp2(S c - lse2), dS = P (dP - delta)
@@ -894,6 +1020,11 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
           pp = 0.f;
           ds = 0.f;
         }
+      }
+      if (DOC) {  // a query of another document contributes nothing
+        const bool same = (dmask >> (16 * qb + i)) & 1u;
+        pp = same ? pp : 0.f;
+        ds = same ? ds : 0.f;
       }
       S[qb][i] = pp;
       dP[qb][i] = ds;
@@ -1025,6 +1156,211 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   }
 }
 
+// D in {64, 128}: the bf16 rounding residuals of P and dS over the query
+// tiles that hold hot queries (see HOT_SPAN), added to the dK, dV that
+// s2a_bwd_dkdv_sw_kernel wrote (same key tiles, so each workgroup owns its
+// keys' rows).  Tiles without hot queries are skipped: without a document
+// mask only the first query tile of a group is hot, and the launch covers
+// only the first key tile.  It is a separate kernel because the pipelined
+// dK/dV kernel has no registers to spare.
+template <int D, bool DOC>
+__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ delta,
+    float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
+  using Dm = BwdDims<D>;
+  constexpr int KP = Dm::KP;
+  constexpr int NCH = KV_BQ * Dm::CPR / THREADS;  // chunks per thread
+  static_assert(KV_BQ * Dm::CPR % THREADS == 0, "tile split");
+  static_assert(KV_BQ == 64, "one tile row per lane in the hot test");
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[KV_BQ * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t dOs[KV_BQ * KP];
+  __shared__ __attribute__((aligned(16))) float lse2s[KV_BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[KV_BQ];
+  __shared__ __attribute__((aligned(16))) int qdocs[KV_BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+  const int tcol = 16 * (grp & 1) + 4 * (lane & 3);
+
+  const UnitTile ut = decode(p, false);
+  if (!ut.ok) return;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
+  const int k0 = ut.tile * KV_BK;
+  if (k0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
+  const int *dbase = DOC ? p.doc + (size_t)ut.b * N : nullptr;
+  const float c2 = p.scale_log2;
+
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + l32;
+  const bool kin = key < glen;
+  const int kpos = kin ? run.pos(key) : 0;
+  const bool kvalid = kin && kpos < L;
+  const int kdoc = DOC ? dbase[kpos] : 0;
+
+  bf16x8 kreg[Dm::KSTEPS], vreg[Dm::KSTEPS];
+  {
+    const size_t off = boff + (size_t)kpos * rs;
+#pragma unroll
+    for (int t = 0; t < Dm::KSTEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (kvalid) {
+        a = *(const u32x4 *)(k + off + 16 * t + 8 * hf);
+        c = *(const u32x4 *)(v + off + 16 * t + 8 * hf);
+      }
+      kreg[t] = __builtin_bit_cast(bf16x8, a);
+      vreg[t] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+
+  f32x16 dkacc[Dm::DB], dvacc[Dm::DB];
+#pragma unroll
+  for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  bool any_hot = false;
+  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
+  for (int it = 0; it < nq; ++it) {
+    const int q0 = k0 + it * KV_BQ;
+    if (!DOC && q0 >= HOT_SPAN) break;
+    // Every wave evaluates the same test, so the branch is uniform across
+    // the workgroup and the barriers below are reached by all waves.
+    const int qsl = q0 + lane;
+    bool h = qsl < glen && qsl < HOT_SPAN;
+    if (DOC && qsl < glen)
+      h |= dbase[run.pos(qsl)] !=
+           dbase[run.pos(qsl >= HOT_SPAN ? qsl - HOT_SPAN : 0)];
+    if (!__any(h)) continue;
+    any_hot = true;
+
+    __syncthreads();  // the previous hot tile's reads are done
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * THREADS;
+      const int r = c / Dm::CPR, ch = c - r * Dm::CPR;
+      const int s = q0 + r;
+      u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+      if (s < glen && ch * 8 < D) {
+        const int qp = run.pos(s);
+        if (qp < L) {
+          const size_t off = boff + (size_t)qp * rs + ch * 8;
+          qv = *(const u32x4 *)(q + off);
+          gv = *(const u32x4 *)(dout + off);
+        }
+      }
+      *(u32x4 *)(Qs + r * KP + ch * 8) = qv;
+      *(u32x4 *)(dOs + r * KP + ch * 8) = gv;
+    }
+    if (tid < KV_BQ) {
+      const int s = q0 + tid;
+      float l2 = INFINITY, dl = 0.f;
+      int dd = 0;
+      if (s < glen) {
+        const int qp = run.pos(s);
+        if (DOC) dd = dbase[qp];
+        if (qp < L) {
+          l2 = lse[lrow + qp] * S2A_LOG2E;
+          dl = delta[lrow + qp];
+        }
+      }
+      lse2s[tid] = l2;
+      dlts[tid] = dl;
+      qdocs[tid] = dd;
+    }
+    __syncthreads();
+
+    if (q0 + KV_BQ - 1 >= kw0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 S, dP;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          S[i] = 0.f;
+          dP[i] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < Dm::KSTEPS; ++t) {
+          const int ro = (32 * qb + l32) * KP + 16 * t + 8 * hf;
+          const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Qs + ro));
+          const bf16x8 ag = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dOs + ro));
+          S = mfma32(aq, kreg[t], S);
+          dP = mfma32(ag, vreg[t], dP);
+        }
+        // residuals x - bf16(x) of the masked P and dS
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = 32 * qb + 8 * i4 + 4 * hf;
+          const f32x4 l2 = *(const f32x4 *)(lse2s + r0);
+          const f32x4 dl = *(const f32x4 *)(dlts + r0);
+          const i32x4 qd = *(const i32x4 *)(qdocs + r0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float pp = __builtin_amdgcn_exp2f(fmaf(S[i], c2, -l2[e]));
+            const float ds = pp * (dP[i] - dl[e]);
+            bool ok = kvalid & (key <= q0 + r0 + e);
+            if (DOC) ok &= qd[e] == kdoc;
+            const float pm = ok ? pp : 0.f, dm = ok ? ds : 0.f;
+            S[i] = pm - (float)(bf16_t)pm;
+            dP[i] = dm - (float)(bf16_t)dm;
+          }
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int e0 = 8 * h2;
+          const bf16x8 pl = to_bf16x8(S[e0], S[e0 + 1], S[e0 + 2], S[e0 + 3],
+                                      S[e0 + 4], S[e0 + 5], S[e0 + 6], S[e0 + 7]);
+          const bf16x8 sl = to_bf16x8(dP[e0], dP[e0 + 1], dP[e0 + 2], dP[e0 + 3],
+                                      dP[e0 + 4], dP[e0 + 5], dP[e0 + 6], dP[e0 + 7]);
+          const int ro = (32 * qb + 16 * h2 + trow) * KP + tcol;
+#pragma unroll
+          for (int db = 0; db < Dm::DB; ++db) {
+            const bf16x8 ag = cat4(lds_read_tr(dOs + ro + 32 * db),
+                                   lds_read_tr(dOs + ro + 8 * KP + 32 * db));
+            dvacc[db] = mfma32(ag, pl, dvacc[db]);
+            const bf16x8 aq = cat4(lds_read_tr(Qs + ro + 32 * db),
+                                   lds_read_tr(Qs + ro + 8 * KP + 32 * db));
+            dkacc[db] = mfma32(aq, sl, dkacc[db]);
+          }
+        }
+      }
+    }
+  }
+
+  if (any_hot && kvalid) {
+    const size_t row = boff + (size_t)kpos * rs;
+#pragma unroll
+    for (int db = 0; db < Dm::DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hf;
+        if (d < D) {
+          f32x4 kk = *(const f32x4 *)(dk + row + d);
+          f32x4 vv = *(const f32x4 *)(dv + row + d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kk[e] += dkacc[db][4 * i4 + e] * p.scale;
+            vv[e] += dvacc[db][4 * i4 + e];
+          }
+          *(f32x4 *)(dk + row + d) = kk;
+          *(f32x4 *)(dv + row + d) = vv;
+        }
+      }
+  }
+}
+
 template <int D, bool OF32>
 hipError_t launch_pre_t(const void *o, const void *dout, float *delta, int B,
                         int N, int H, hipStream_t st) {
@@ -1044,8 +1380,8 @@ dim3 unit_grid(const S2AParams &p, int rows_per_wg) {
   return dim3((unsigned)units_pad * (unsigned)tiles);
 }
 
-template <int D>
-hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
+template <int D, bool DOC>
+hipError_t launch_dkdv_d(const void *q, const void *k, const void *v,
                          const void *dout, const float *lse,
                          const float *delta, float *dk, float *dv,
                          S2AParams p, hipStream_t st) {
@@ -1055,14 +1391,39 @@ hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
   void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
                   (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
                   (void *)&p};
-  const void *fn = D >= 64
-                       ? (const void *)s2a_bwd_dkdv_sw_kernel<(D >= 64 ? D : 64), KV_BQ, 2>
-                       : (const void *)s2a_bwd_dkdv_kernel<D>;
-  return hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+  const void *fn;
+  if constexpr (D >= 64)
+    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, 2, DOC>;
+  else
+    fn = (const void *)s2a_bwd_dkdv_kernel<D, DOC>;
+  hipError_t e = hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+  if constexpr (D >= 64) {
+    // the sw kernel rounds P and dS to bf16 everywhere; add the residuals
+    // of the hot tiles (the generic kernel does so inline).  Without a
+    // document mask only key tile 0 of each group meets hot queries.
+    if (e != hipSuccess) return e;
+    dim3 grid = unit_grid(p, KV_BK);
+    if (!DOC) {
+      p.tiles = 1;
+      grid = dim3((unsigned)((p.units + 7) / 8 * 8));
+    }
+    e = hipLaunchKernel((const void *)s2a_bwd_dkdv_lo_kernel<D, DOC>, grid,
+                        dim3(THREADS), args, 0, st);
+  }
+  return e;
 }
 
 template <int D>
-hipError_t launch_dq_t(const void *q, const void *k, const void *v,
+hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
+                         const void *dout, const float *lse,
+                         const float *delta, float *dk, float *dv,
+                         const S2AParams &p, hipStream_t st) {
+  return p.doc ? launch_dkdv_d<D, true>(q, k, v, dout, lse, delta, dk, dv, p, st)
+               : launch_dkdv_d<D, false>(q, k, v, dout, lse, delta, dk, dv, p, st);
+}
+
+template <int D, bool DOC>
+hipError_t launch_dq_d(const void *q, const void *k, const void *v,
                        const void *dout, const float *lse, const float *delta,
                        float *dq, S2AParams p, hipStream_t st) {
   p.tiles = (p.g.G + DQ_BQ - 1) / DQ_BQ;
@@ -1070,10 +1431,20 @@ hipError_t launch_dq_t(const void *q, const void *k, const void *v,
                *vv = (const bf16_t *)v, *gg = (const bf16_t *)dout;
   void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
                   (void *)&lse, (void *)&delta, (void *)&dq, (void *)&p};
-  const void *fn = D >= 64
-                       ? (const void *)s2a_bwd_dq_sw_kernel<(D >= 64 ? D : 64)>
-                       : (const void *)s2a_bwd_dq_kernel<D>;
+  const void *fn;
+  if constexpr (D >= 64)
+    fn = (const void *)s2a_bwd_dq_sw_kernel<D, DOC>;
+  else
+    fn = (const void *)s2a_bwd_dq_kernel<D, DOC>;
   return hipLaunchKernel(fn, unit_grid(p, DQ_BQ), dim3(DQ_THREADS), args, 0, st);
+}
+
+template <int D>
+hipError_t launch_dq_t(const void *q, const void *k, const void *v,
+                       const void *dout, const float *lse, const float *delta,
+                       float *dq, const S2AParams &p, hipStream_t st) {
+  return p.doc ? launch_dq_d<D, true>(q, k, v, dout, lse, delta, dq, p, st)
+               : launch_dq_d<D, false>(q, k, v, dout, lse, delta, dq, p, st);
 }
 
 }  // namespace

@@ -14,6 +14,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define S2A_LOG2E 1.4426950408889634f
 #define S2A_LN2 0.6931471805599453f
@@ -27,6 +28,7 @@ struct S2AParams {
   int units;      // B * H * ngmax
   float scale;    // softmax scale
   float scale_log2;  // scale * log2(e)
+  const int *doc; // document IDs [B, N] (nullptr: no document mask)
 };
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (checked on

@@ -40,7 +40,7 @@ struct FwdDims {
   static constexpr int CPR = DP / 8;          // 16-byte chunks per row
 };
 
-template <int D, bool OF32>
+template <int D, bool OF32, bool DOC>
 __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   // Two K and two V buffers: tile t+1 is written while tile t is read.
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2 * TILE];
+  __shared__ __attribute__((aligned(16))) int kdoc[2][FWD_BK];  // DOC only
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   const bool qin = qslot < glen;
   const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
+  const int qdoc = DOC ? p.doc[(size_t)b * N + qpos] : 0;
 
   bf16x8 qreg[Dm::KSTEPS];
   {
@@ -100,7 +102,12 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   // c / CPR, 16-byte column c % CPR.  Rows outside the group or at padded
   // positions are zero.
   u32x4 kst[NCH], vst[NCH];
+  int kdst = 0;  // document ID of key k0 + tid (DOC, tid < FWD_BK)
   auto fetch = [&](int k0) {
+    if (DOC && tid < FWD_BK) {
+      const int ks = k0 + tid;
+      kdst = p.doc[(size_t)b * N + (ks < glen ? run.pos(ks) : 0)];
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * FWD_THREADS;
@@ -120,6 +127,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
     }
   };
   auto stage = [&](int buf) {
+    if (DOC && tid < FWD_BK) kdoc[buf][tid] = kdst;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = tid + i * FWD_THREADS;
@@ -178,19 +186,27 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
         }
       }
 
-      // Mask where the tile crosses the diagonal, the group end or padding.
+      // Mask where the tile crosses the diagonal, the group end or padding
+      // (and everywhere under a document mask).
       const int kstop = min(k0 + FWD_BK, glen);
-      const bool edge = (k0 + FWD_BK - 1 > wq_lo) || (k0 + FWD_BK > glen) ||
+      const bool edge = DOC || (k0 + FWD_BK - 1 > wq_lo) ||
+                        (k0 + FWD_BK > glen) ||
                         s2a_range_has_padding(run, k0, kstop, N, L);
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool ok =
-                ks <= qslot && ks < glen && run.pos(ks) < L;
-            if (!ok) sacc[kb][i] = -INFINITY;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            i32x4 kd = {0, 0, 0, 0};
+            if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * g4 + j;
+              const int ks = k0 + 32 * kb + 8 * g4 + 4 * hf + j;
+              bool ok = (ks <= qslot) & (ks < glen) & (run.pos(ks) < L);
+              if (DOC) ok &= kd[j] == qdoc;
+              sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+            }
           }
       }
 
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
 // Forward for D in {64, 128}: same math as s2a_fwd_kernel, with K/V tiles
 // in the swizzled unpadded layout of s2a_tile.h filled by direct
 // global -> LDS loads (no staging registers, addresses precomputed).
-template <int D, bool OF32>
+template <int D, bool OF32, bool DOC>
 __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
@@ -292,6 +308,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = FWD_BK * T::ROWB;  // bytes per tile buffer
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  __shared__ __attribute__((aligned(16))) int kdoc[2][FWD_BK];  // DOC only
   char *const Ks = smem;              // two K buffers
   char *const Vs = smem + 2 * TILEB;  // two V buffers
 
@@ -323,6 +340,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   const bool qin = qslot < glen;
   const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
+  const int qdoc = DOC ? p.doc[(size_t)b * N + qpos] : 0;
 
   bf16x8 qreg[KSTEPS];
   {
@@ -347,6 +365,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     } else {
       ld.general(kbh, rs, run, glen, k0, L, kd);
       ld.general(vbh, rs, run, glen, k0, L, vd);
+    }
+    if (DOC && w == 0) {  // document IDs of the tile's 64 keys
+      const int ks = k0 + lane;
+      g2lds4(p.doc + (size_t)b * N + (ks < glen ? run.pos(ks) : 0),
+             &kdoc[buf][0]);
     }
   };
 
@@ -407,17 +430,23 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
         for (int t = 0; t < KSTEPS; ++t) sacc[kb] = mfma32(a[t], qreg[t], sacc[kb]);
       }
 
-      const bool edge = (k0 + FWD_BK - 1 > wq_lo) ||
+      const bool edge = DOC || (k0 + FWD_BK - 1 > wq_lo) ||
                         !tile_plain(run, glen, k0, FWD_BK, L);
       if (edge) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ks = k0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool ok =
-                ks <= qslot && ks < glen && run.pos(ks) < L;
-            if (!ok) sacc[kb][i] = -INFINITY;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            i32x4 kd = {0, 0, 0, 0};
+            if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * g4 + j;
+              const int ks = k0 + 32 * kb + 8 * g4 + 4 * hf + j;
+              bool ok = (ks <= qslot) & (ks < glen) & (run.pos(ks) < L);
+              if (DOC) ok &= kd[j] == qdoc;
+              sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+            }
           }
       }
 
@@ -500,8 +529,8 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   }
 }
 
-template <int D, bool OF32>
-hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
+template <int D, bool OF32, bool DOC>
+hipError_t launch_fwd_d(const void *q, const void *k, const void *v, void *o,
                         float *lse, const S2AParams &p, hipStream_t st) {
   const int units_pad = (p.units + 7) / 8 * 8;
   const bf16_t *qq = (const bf16_t *)q, *kk = (const bf16_t *)k,
@@ -510,9 +539,19 @@ hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
   void *args[] = {(void *)&qq, (void *)&kk, (void *)&vv, (void *)&o,
                   (void *)&lse, (void *)&pp};
   dim3 grid((unsigned)units_pad * (unsigned)p.tiles);
-  const void *fn = D >= 64 ? (const void *)s2a_fwd_sw_kernel<(D >= 64 ? D : 64), OF32>
-                           : (const void *)s2a_fwd_kernel<D, OF32>;
+  const void *fn;
+  if constexpr (D >= 64)
+    fn = (const void *)s2a_fwd_sw_kernel<D, OF32, DOC>;
+  else
+    fn = (const void *)s2a_fwd_kernel<D, OF32, DOC>;
   return hipLaunchKernel(fn, grid, dim3(FWD_THREADS), args, 0, st);
+}
+
+template <int D, bool OF32>
+hipError_t launch_fwd_t(const void *q, const void *k, const void *v, void *o,
+                        float *lse, const S2AParams &p, hipStream_t st) {
+  return p.doc ? launch_fwd_d<D, OF32, true>(q, k, v, o, lse, p, st)
+               : launch_fwd_d<D, OF32, false>(q, k, v, o, lse, p, st);
 }
 
 }  // namespace

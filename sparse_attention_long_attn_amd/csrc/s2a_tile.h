@@ -38,6 +38,13 @@ __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave) {
       gptr, (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
 }
 
+// Direct global -> LDS copy of 4 bytes per lane (lane i lands at byte 4*i
+// past lds_wave, which must be the same for every lane of the wave).
+__device__ __forceinline__ void g2lds4(const void *gptr, void *lds_wave) {
+  __builtin_amdgcn_global_load_lds(
+      gptr, (__attribute__((address_space(3))) void *)lds_wave, 4, 0, 0);
+}
+
 // Loader of one ROWS-row tile of a [B,N,H,D] tensor by NWAVES waves.  Each
 // wave issues IPW instructions; instruction i of wave w fills tile chunks
 // [(w*IPW + i)*64, +64).  Per lane it keeps the tile row it fills and the

@@ -50,10 +50,23 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _docs(doc_ids, q):
+    """Device pointer of optional int32 [B, N] document IDs (None: none)."""
+    if doc_ids is None:
+        return None
+    B, N = q.shape[0], q.shape[1]
+    if doc_ids.dtype != torch.int32 or tuple(doc_ids.shape) != (B, N) \
+            or not doc_ids.is_contiguous() or doc_ids.device != q.device:
+        raise ValueError("doc_ids must be a contiguous int32 [B, N] tensor on "
+                         "the device of q")
+    return doc_ids.data_ptr()
+
+
 def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
         valid_len: int | None = None, scale: float | None = None,
-        out_dtype=torch.float32, o=None, lse=None):
-    """S²-Attn forward.  Returns (o [B,N,H,D], lse [B,H,N] float32)."""
+        out_dtype=torch.float32, o=None, lse=None, doc_ids=None):
+    """S²-Attn forward.  Returns (o [B,N,H,D], lse [B,H,N] float32).
+    doc_ids: optional int32 [B, N] document IDs of packed samples."""
     B, N, H, D = _check_qkv(q, k, v)
     shift = G // 2 if shift is None else shift
     valid_len = N if valid_len is None else valid_len
@@ -72,14 +85,15 @@ def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
     lib = _lib.load()
     _lib.check(lib.s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
                               _ptr(lse), B, N, H, D, G, shift,
-                              _boundary(boundary), valid_len, scale,
-                              _stream(q.device)))
+                              _boundary(boundary), valid_len,
+                              _docs(doc_ids, q), scale, _stream(q.device)))
     return o, lse
 
 
 def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
         boundary="wrap", valid_len: int | None = None,
-        scale: float | None = None, dq=None, dk=None, dv=None, delta=None):
+        scale: float | None = None, dq=None, dk=None, dv=None, delta=None,
+        doc_ids=None):
     """S²-Attn backward from the forward's o and lse.
     Returns (dq, dk, dv), float32 [B,N,H,D]."""
     B, N, H, D = _check_qkv(q, k, v, dout)
@@ -105,8 +119,8 @@ def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
     _lib.check(lib.s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
                               _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                               _ptr(dv), _ptr(delta), B, N, H, D, G, shift,
-                              _boundary(boundary), valid_len, scale,
-                              _stream(q.device)))
+                              _boundary(boundary), valid_len,
+                              _docs(doc_ids, q), scale, _stream(q.device)))
     return dq, dk, dv
 
 
@@ -130,7 +144,8 @@ def _stage_args(q, G, shift, valid_len, scale):
 
 def bwd_dkdv(q, k, v, lse, delta, dout, dk, dv, *, G: int,
              shift: int | None = None, boundary="wrap",
-             valid_len: int | None = None, scale: float | None = None):
+             valid_len: int | None = None, scale: float | None = None,
+             doc_ids=None):
     """dK/dV stage (needs delta from bwd_preprocess)."""
     _check_qkv(q, k, v, dout)
     B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
@@ -139,13 +154,15 @@ def bwd_dkdv(q, k, v, lse, delta, dout, dk, dv, *, G: int,
     _lib.check(lib.s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
                                    _ptr(delta), _ptr(dout), _ptr(dk),
                                    _ptr(dv), B, N, H, D, G, shift,
-                                   _boundary(boundary), valid_len, scale,
+                                   _boundary(boundary), valid_len,
+                                   _docs(doc_ids, q), scale,
                                    _stream(q.device)))
 
 
 def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
            shift: int | None = None, boundary="wrap",
-           valid_len: int | None = None, scale: float | None = None):
+           valid_len: int | None = None, scale: float | None = None,
+           doc_ids=None):
     """dQ stage (needs delta from bwd_preprocess)."""
     _check_qkv(q, k, v, dout)
     B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
@@ -154,7 +171,7 @@ def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
     _lib.check(lib.s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
                                  _ptr(delta), _ptr(dout), _ptr(dq), B, N, H,
                                  D, G, shift, _boundary(boundary), valid_len,
-                                 scale, _stream(q.device)))
+                                 _docs(doc_ids, q), scale, _stream(q.device)))
 
 
 def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
@@ -175,26 +192,28 @@ class S2AttnFunction(torch.autograd.Function):
     """Autograd wrapper: forward and backward both run in the library."""
 
     @staticmethod
-    def forward(ctx, q, k, v, G, shift, boundary, valid_len, scale):
+    def forward(ctx, q, k, v, G, shift, boundary, valid_len, scale,
+                doc_ids=None):
         o, lse = fwd(q, k, v, G=G, shift=shift, boundary=boundary,
-                     valid_len=valid_len, scale=scale)
+                     valid_len=valid_len, scale=scale, doc_ids=doc_ids)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (G, shift, boundary, valid_len, scale)
+        ctx.cfg = (G, shift, boundary, valid_len, scale, doc_ids)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        G, shift, boundary, valid_len, scale = ctx.cfg
+        G, shift, boundary, valid_len, scale, doc_ids = ctx.cfg
         dq, dk, dv = bwd(q, k, v, o, lse,
                          do.to(torch.bfloat16).contiguous(), G=G,
                          shift=shift, boundary=boundary, valid_len=valid_len,
-                         scale=scale)
+                         scale=scale, doc_ids=doc_ids)
         return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype),
-                None, None, None, None, None)
+                None, None, None, None, None, None)
 
 
 def s2_attention(q, k, v, G, shift=None, boundary="wrap", valid_len=None,
-                 scale=None):
+                 scale=None, doc_ids=None):
     """Differentiable S²-Attn (float32 output)."""
-    return S2AttnFunction.apply(q, k, v, G, shift, boundary, valid_len, scale)
+    return S2AttnFunction.apply(q, k, v, G, shift, boundary, valid_len, scale,
+                                doc_ids)

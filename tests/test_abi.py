@@ -43,7 +43,7 @@ def call_fwd(**kw):
     lib = _lib.load()
     return lib.s2attn_fwd(NULL, NULL, NULL, NULL, 1, NULL, a["B"], a["N"],
                           a["H"], a["D"], a["G"], a["shift"], a["boundary"],
-                          a["L"], a["scale"], NULL)
+                          a["L"], a.get("doc"), a["scale"], NULL)
 
 
 def call_bwd(**kw):
@@ -51,7 +51,8 @@ def call_bwd(**kw):
     lib = _lib.load()
     return lib.s2attn_bwd(NULL, NULL, NULL, NULL, 1, NULL, NULL, NULL, NULL,
                           NULL, NULL, a["B"], a["N"], a["H"], a["D"], a["G"],
-                          a["shift"], a["boundary"], a["L"], a["scale"], NULL)
+                          a["shift"], a["boundary"], a["L"], a.get("doc"),
+                          a["scale"], NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -66,6 +67,7 @@ def call_bwd(**kw):
     (dict(D=24), _lib.S2A_EUNSUPPORTED),
     (dict(D=256), _lib.S2A_EUNSUPPORTED),
     (dict(H=1 << 17, D=128), _lib.S2A_EUNSUPPORTED),   # H*D = 2^24
+    (dict(doc=6), _lib.S2A_EINVAL),                    # misaligned doc IDs
     (dict(), _lib.S2A_EINVAL),          # valid shape, NULL pointers
 ])
 @pytest.mark.parametrize("call", [call_fwd, call_bwd])
@@ -80,11 +82,11 @@ def test_misaligned_pointer_rejected():
     base = ctypes.addressof(buf)
     p = ((base + 15) // 16) * 16
     st = lib.s2attn_fwd(p + 2, p, p, p, 1, p, 1, 64, 4, 16, 16, 8, 0, 64,
-                        0.25, None)
+                        None, 0.25, None)
     assert st == _lib.S2A_EINVAL
     assert "aligned" in lib.s2attn_last_error().decode()
     st = lib.s2attn_fwd(p, p, p, p, 1, p, 1, 64, 4, 16, 16, 8, 0, 64,
-                        float("nan"), None)
+                        None, float("nan"), None)
     assert st == _lib.S2A_EINVAL
 
 
