@@ -16,7 +16,9 @@ from the definitions on the page "4.1.2 Â· LongLoRA: ç”¨SÂ²-Attnå®Œæˆé•¿ä¸Šä¸‹æ
   Â§1 ("Reshapeå¦‚ä½•å¤ç”¨æ™®é€škernel"), derivation B, written independently;
 * ``forward`` / ``backward`` -- dense masked softmax attention over the
   derivation-A adjacency (Â§3, equation for o_i^s and the gradient
-  equation for dL/dz_j).
+  equation for dL/dz_j);
+* ``rope`` -- rotary position embedding at global positions with linear
+  position interpolation (Â§3.1, the rotation R(m, w); Â§1.1 on position IDs).
 
 Every function is pinned by tests against things other than itself (worked
 examples printed on the pages, closed-form pair counts, G=N reducing to
@@ -28,3 +30,4 @@ from .s2attn_oracle import (  # noqa: F401
     group_maps_b, adjacency_block, adjacency_dense, allowed_pairs, forward,
     backward, forward_segments, backward_segments, segments,
 )
+from .rope import HALF, INTERLEAVED, frequencies, rope  # noqa: F401
