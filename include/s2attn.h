@@ -161,6 +161,42 @@ s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
                             int valid_len, int *gid, int *slot, int *src,
                             void *stream);
 
+/*
+ * Rotary position embedding (RoPE) at global positions: the prologue that
+ * turns projected q and k into the rotated q and k the attention calls
+ * take.  For pair i of every head (i = 0 .. D/2-1) at token (b, n):
+ *   m      = pos_scale * (pos_ids ? pos_ids[b*N + n] : n)
+ *   w_i    = base^(-2i/D)
+ *   (y_a, y_b) = (cos(m w_i) x_a - sin(m w_i) x_b,
+ *                 sin(m w_i) x_a + cos(m w_i) x_b)
+ * with channels (a, b) = (i, i + D/2) for S2A_ROPE_HALF (the Llama layout)
+ * or (2i, 2i + 1) for S2A_ROPE_INTERLEAVED.  The rotation is the R(m, w) of
+ * PaperTrace LongLoRA §3.1; m is the token's original position ID -- the
+ * shift of the grouped heads only permutes tensors -- and linear position
+ * interpolation is pos_scale = L0 / L1 (§1.1, the paragraphs on RoPE and
+ * position interpolation).  The frequency schedule and the pairing are not
+ * fixed by the pages; these are the conventions of the Llama models the
+ * pages fine-tune.
+ *
+ * s2attn_rope:      x, y bf16 [B, N, H, D]; y = R x, angles formed in
+ *                   double precision, the rotation in fp32, rounded once.
+ * s2attn_rope_bwd:  gy, gx f32 [B, N, H, D]; gx = R^T gy (the gradient of
+ *                   s2attn_rope with respect to x, given that of y).
+ * pos_ids: NULL or int32 [B, N] (4-byte aligned); y may equal x and gx may
+ * equal gy (in place).  Checks: sizes > 0, D in {16, 32, 64, 128}
+ * (S2A_EUNSUPPORTED otherwise), pointers non-NULL and 16-byte aligned,
+ * base and pos_scale positive and finite, pairing one of the two values.
+ */
+typedef enum { S2A_ROPE_HALF = 0, S2A_ROPE_INTERLEAVED = 1 } s2a_rope_pairing;
+
+s2a_status s2attn_rope(const void *x, void *y, int B, int N, int H, int D,
+                       const int *pos_ids, float base, float pos_scale,
+                       int pairing, void *stream);
+
+s2a_status s2attn_rope_bwd(const float *gy, float *gx, int B, int N, int H,
+                           int D, const int *pos_ids, float base,
+                           float pos_scale, int pairing, void *stream);
+
 /* Static description of a status code. */
 const char *s2attn_strerror(int status);
 

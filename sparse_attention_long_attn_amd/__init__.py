@@ -7,8 +7,9 @@ marshals torch tensors into its calls.
 from . import _lib, work  # noqa: F401
 from ._lib import S2A_WRAP, S2A_SPLIT, S2AttnError, load  # noqa: F401
 from .ops import (fwd, bwd, bwd_preprocess, bwd_dkdv, bwd_dq,  # noqa: F401
-                  group_map, s2_attention, S2AttnFunction)
+                  group_map, rope, rope_bwd, s2_attention, S2AttnFunction)
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv",
-           "bwd_dq", "group_map", "s2_attention", "S2AttnFunction",
+           "bwd_dq", "group_map", "rope", "rope_bwd", "s2_attention",
+           "S2AttnFunction",
            "S2A_WRAP", "S2A_SPLIT", "S2AttnError", "load", "work"]

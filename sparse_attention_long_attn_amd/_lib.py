@@ -15,9 +15,11 @@ LIB_PATH = os.path.join(_PKG, "libs2attn.so")
 S2A_OK, S2A_EINVAL, S2A_EUNSUPPORTED, S2A_EHIP = 0, 1, 2, 3
 S2A_WRAP, S2A_SPLIT, S2A_CYCLIC = 0, 1, 2
 S2A_BF16, S2A_F32 = 0, 1
+S2A_ROPE_HALF, S2A_ROPE_INTERLEAVED = 0, 1
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
            "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_group_map",
+           "s2attn_rope", "s2attn_rope_bwd",
            "s2attn_strerror", "s2attn_last_error", "s2attn_version")
 
 _lib = None
@@ -55,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd_dq.restype = I
     lib.s2attn_group_map.argtypes = [I, I, I, I, I, P, P, P, P]
     lib.s2attn_group_map.restype = I
+    # x, y, B, N, H, D, pos_ids, base, pos_scale, pairing, stream
+    for fn in (lib.s2attn_rope, lib.s2attn_rope_bwd):
+        fn.argtypes = [P, P, I, I, I, I, P, F, F, I, P]
+        fn.restype = I
     lib.s2attn_strerror.argtypes = [I]
     lib.s2attn_strerror.restype = ctypes.c_char_p
     lib.s2attn_last_error.argtypes = []

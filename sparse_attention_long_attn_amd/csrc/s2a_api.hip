@@ -218,6 +218,63 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
                     "dQ launch");
 }
 
+namespace {
+
+s2a_status rope_common(const void *x, void *y, int B, int N, int H, int D,
+                       const int *pos_ids, float base, float pos_scale,
+                       int pairing) {
+  if (B <= 0 || N <= 0 || H <= 0 || D <= 0)
+    return fail(S2A_EINVAL, "sizes must be positive");
+  if (D != 16 && D != 32 && D != 64 && D != 128)
+    return fail(S2A_EUNSUPPORTED, "head width D=%lld not in {16,32,64,128}", D);
+  if ((long long)B * N > (1ll << 31))
+    return fail(S2A_EINVAL, "B*N=%lld too large for one launch",
+                (long long)B * N);
+  if (!x || !y) return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(y))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (!aligned4(pos_ids))
+    return fail(S2A_EINVAL, "pos_ids must be 4-byte aligned");
+  if (!(base > 0.f) || !isfinite(base))
+    return fail(S2A_EINVAL, "base must be positive and finite");
+  if (!(pos_scale > 0.f) || !isfinite(pos_scale))
+    return fail(S2A_EINVAL, "pos_scale must be positive and finite");
+  if (pairing != S2A_ROPE_HALF && pairing != S2A_ROPE_INTERLEAVED)
+    return fail(S2A_EINVAL, "pairing=%lld is neither HALF nor INTERLEAVED",
+                pairing);
+  return S2A_OK;
+}
+
+}  // namespace
+
+s2a_status s2attn_rope(const void *x, void *y, int B, int N, int H, int D,
+                       const int *pos_ids, float base, float pos_scale,
+                       int pairing, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = rope_common(x, y, B, N, H, D, pos_ids, base, pos_scale,
+                              pairing);
+  if (st != S2A_OK) return st;
+  return hip_status(s2a_launch_rope(x, y, false, false, B, N, H, D, pos_ids,
+                                    base, pos_scale,
+                                    pairing == S2A_ROPE_HALF,
+                                    (hipStream_t)stream),
+                    "rope launch");
+}
+
+s2a_status s2attn_rope_bwd(const float *gy, float *gx, int B, int N, int H,
+                           int D, const int *pos_ids, float base,
+                           float pos_scale, int pairing, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = rope_common(gy, gx, B, N, H, D, pos_ids, base, pos_scale,
+                              pairing);
+  if (st != S2A_OK) return st;
+  return hip_status(s2a_launch_rope(gy, gx, true, true, B, N, H, D, pos_ids,
+                                    base, pos_scale,
+                                    pairing == S2A_ROPE_HALF,
+                                    (hipStream_t)stream),
+                    "rope backward launch");
+}
+
 s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
                             int valid_len, int *gid, int *slot, int *src,
                             void *stream) {

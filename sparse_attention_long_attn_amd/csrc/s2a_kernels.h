@@ -34,3 +34,8 @@ hipError_t s2a_launch_bwd_dq(const void *q, const void *k, const void *v,
 
 hipError_t s2a_launch_map(const S2AGeom &g, int *gid, int *slot, int *src,
                           hipStream_t st);
+
+hipError_t s2a_launch_rope(const void *x, void *y, bool f32, bool inverse,
+                           int B, int N, int H, int D, const int *pos,
+                           float base, float pscale, bool half,
+                           hipStream_t st);

@@ -174,6 +174,63 @@ def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
                                  _docs(doc_ids, q), scale, _stream(q.device)))
 
 
+PAIRINGS = {"half": _lib.S2A_ROPE_HALF, "interleaved": _lib.S2A_ROPE_INTERLEAVED,
+            _lib.S2A_ROPE_HALF: _lib.S2A_ROPE_HALF,
+            _lib.S2A_ROPE_INTERLEAVED: _lib.S2A_ROPE_INTERLEAVED}
+
+
+def _rope_args(x, pos_ids, pairing):
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, N, H, D] GPU tensor")
+    B, N, H, D = x.shape
+    pp = None
+    if pos_ids is not None:
+        if pos_ids.dtype != torch.int32 or tuple(pos_ids.shape) != (B, N) \
+                or not pos_ids.is_contiguous() or pos_ids.device != x.device:
+            raise ValueError("pos_ids must be a contiguous int32 [B, N] "
+                             "tensor on the device of x")
+        pp = pos_ids.data_ptr()
+    try:
+        pr = PAIRINGS[pairing]
+    except KeyError:
+        raise ValueError(f"pairing must be 'half' or 'interleaved', got "
+                         f"{pairing!r}")
+    return B, N, H, D, pp, pr
+
+
+def rope(x, *, base: float = 10000.0, pos_scale: float = 1.0, pos_ids=None,
+         pairing="half", out=None):
+    """Rotary position embedding of bf16 [B,N,H,D] at global positions
+    (pos_ids int32 [B,N], default 0..N-1), scaled by pos_scale (linear
+    position interpolation).  out may be x (in place)."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    B, N, H, D, pp, pr = _rope_args(x, pos_ids, pairing)
+    out = torch.empty_like(x) if out is None else out
+    if out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor like x")
+    lib = _lib.load()
+    _lib.check(lib.s2attn_rope(_ptr(x), _ptr(out), B, N, H, D, pp, base,
+                               pos_scale, pr, _stream(x.device)))
+    return out
+
+
+def rope_bwd(gy, *, base: float = 10000.0, pos_scale: float = 1.0,
+             pos_ids=None, pairing="half", out=None):
+    """Gradient of rope(): R^T applied to float32 [B,N,H,D] gradients.
+    out may be gy (in place)."""
+    if gy.dtype != torch.float32:
+        raise ValueError("gy must be float32")
+    B, N, H, D, pp, pr = _rope_args(gy, pos_ids, pairing)
+    out = torch.empty_like(gy) if out is None else out
+    if out.dtype != torch.float32 or out.shape != gy.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor like gy")
+    lib = _lib.load()
+    _lib.check(lib.s2attn_rope_bwd(_ptr(gy), _ptr(out), B, N, H, D, pp, base,
+                                   pos_scale, pr, _stream(gy.device)))
+    return out
+
+
 def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
               valid_len: int | None = None, device="cuda"):
     """Group index maps (gid, slot, src), each int32 [2, N] on the device."""
@@ -189,31 +246,42 @@ def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
 
 
 class S2AttnFunction(torch.autograd.Function):
-    """Autograd wrapper: forward and backward both run in the library."""
+    """Autograd wrapper: forward and backward both run in the library.
+    With rope (a dict of rope() keywords) q and k are the unrotated
+    projections: they are rotated at their global positions first, and the
+    gradients are rotated back."""
 
     @staticmethod
     def forward(ctx, q, k, v, G, shift, boundary, valid_len, scale,
-                doc_ids=None):
+                doc_ids=None, rope_cfg=None):
+        if rope_cfg is not None:
+            q = rope(q, **rope_cfg)
+            k = rope(k, **rope_cfg)
         o, lse = fwd(q, k, v, G=G, shift=shift, boundary=boundary,
                      valid_len=valid_len, scale=scale, doc_ids=doc_ids)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (G, shift, boundary, valid_len, scale, doc_ids)
+        ctx.cfg = (G, shift, boundary, valid_len, scale, doc_ids, rope_cfg)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        G, shift, boundary, valid_len, scale, doc_ids = ctx.cfg
+        G, shift, boundary, valid_len, scale, doc_ids, rope_cfg = ctx.cfg
         dq, dk, dv = bwd(q, k, v, o, lse,
                          do.to(torch.bfloat16).contiguous(), G=G,
                          shift=shift, boundary=boundary, valid_len=valid_len,
                          scale=scale, doc_ids=doc_ids)
+        if rope_cfg is not None:
+            rope_bwd(dq, out=dq, **rope_cfg)
+            rope_bwd(dk, out=dk, **rope_cfg)
         return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype),
-                None, None, None, None, None, None)
+                None, None, None, None, None, None, None)
 
 
 def s2_attention(q, k, v, G, shift=None, boundary="wrap", valid_len=None,
-                 scale=None, doc_ids=None):
-    """Differentiable S²-Attn (float32 output)."""
+                 scale=None, doc_ids=None, rope_cfg=None):
+    """Differentiable S²-Attn (float32 output).  rope_cfg: None, or a dict
+    of rope() keywords (base, pos_scale, pos_ids, pairing) to rotate q and
+    k at their global positions inside the op."""
     return S2AttnFunction.apply(q, k, v, G, shift, boundary, valid_len, scale,
-                                doc_ids)
+                                doc_ids, rope_cfg)

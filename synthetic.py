@@ -119,5 +119,20 @@ def make_doc_ids(seed: int, B: int, N: int, mean_len: int,
     return out
 
 
+def doc_positions(doc: np.ndarray) -> np.ndarray:
+    """Position IDs of packed samples: int32 [B, N], restarting at 0 where
+    the document ID changes (each packed sample keeps its own positions)."""
+    doc = np.asarray(doc)
+    B, N = doc.shape
+    out = np.empty((B, N), np.int32)
+    for b in range(B):
+        start = 0
+        for x in range(N):
+            if x and doc[b, x] != doc[b, x - 1]:
+                start = x
+            out[b, x] = x - start
+    return out
+
+
 def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)

@@ -62,7 +62,7 @@ def call_bwd(**kw):
     (dict(L=0), _lib.S2A_EINVAL),
     (dict(L=65), _lib.S2A_EINVAL),
     (dict(shift=4), _lib.S2A_EINVAL),
-    (dict(boundary=2), _lib.S2A_EINVAL),
+    (dict(boundary=3), _lib.S2A_EINVAL),
     (dict(B=0), _lib.S2A_EINVAL),
     (dict(D=24), _lib.S2A_EUNSUPPORTED),
     (dict(D=256), _lib.S2A_EUNSUPPORTED),
@@ -88,6 +88,29 @@ def test_misaligned_pointer_rejected():
     st = lib.s2attn_fwd(p, p, p, p, 1, p, 1, 64, 4, 16, 16, 8, 0, 64,
                         None, float("nan"), None)
     assert st == _lib.S2A_EINVAL
+
+
+def test_rope_rejects_bad_arguments():
+    lib = _lib.load()
+    buf = (ctypes.c_char * 4096)()
+    p = ((ctypes.addressof(buf) + 15) // 16) * 16
+    ok = dict(x=p, y=p, B=1, N=4, H=2, D=16, pos=None, base=10000.0,
+              ps=1.0, pairing=0)
+    bad = [
+        dict(x=None), dict(y=p + 8), dict(B=0), dict(D=24),
+        dict(D=256), dict(pos=p + 2), dict(base=0.0),
+        dict(base=float("inf")), dict(ps=-1.0), dict(ps=float("nan")),
+        dict(pairing=2),
+    ]
+    for fn in (lib.s2attn_rope, lib.s2attn_rope_bwd):
+        for kw in bad:
+            a = dict(ok, **kw)
+            st = fn(a["x"], a["y"], a["B"], a["N"], a["H"], a["D"], a["pos"],
+                    a["base"], a["ps"], a["pairing"], None)
+            want = (_lib.S2A_EUNSUPPORTED if kw.get("D") in (24, 256)
+                    else _lib.S2A_EINVAL)
+            assert st == want, kw
+            assert lib.s2attn_last_error().decode() != ""
 
 
 def test_group_map_rejects_bad_shapes():
