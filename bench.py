@@ -45,6 +45,11 @@ def parse():
                          "B=2 N=12288 H=32 D=128 for every G with shift 0 and "
                          "shift G/2 under each boundary variant (one JSON line "
                          "per entry)")
+    ap.add_argument("--rope", action="store_true",
+                    help="instead of the headline line, time the RoPE "
+                         "prologue (rotate q and k, bf16) and its gradient "
+                         "map (dq and dk, fp32, in place) at the headline "
+                         "shape (one JSON line, HBM roofline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a plain copy "
                          "kernel of known size, to calibrate HBM counters)")
@@ -171,6 +176,65 @@ def sweep(args):
             }), flush=True)
 
 
+def rope_bench(args):
+    """The RoPE prologue at the headline shape: two rope launches (q, k;
+    bf16 in and out) and two rope_bwd launches (dq, dk; fp32, in place),
+    each timed with HIP events.  Each launch streams its tensor once, so
+    the algorithmic bytes are one read and one write of it."""
+    import torch
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    cfg = WORKLOAD
+    B, N, H, D = (cfg[k] for k in ("B", "N", "H", "D"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ins = syn.make_inputs(cfg["config"], 0, B, N, H, D)
+    q, k = (torch.from_numpy(ins[t].view("int16")).view(torch.bfloat16)
+            .to(dev) for t in ("q", "k"))
+    del ins
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    g = [torch.randn((B, N, H, D), device=dev) for _ in range(2)]
+    rcfg = dict(base=10000.0, pos_scale=1.0, pairing="half")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    fwd_ms = timed(lambda: (s2a.rope(q, out=qr, **rcfg),
+                            s2a.rope(k, out=kr, **rcfg))) / 2
+    bwd_ms = timed(lambda: (s2a.rope_bwd(g[0], out=g[0], **rcfg),
+                            s2a.rope_bwd(g[1], out=g[1], **rcfg))) / 2
+    elems = B * N * H * D
+    fb, bb = 2 * 2 * elems, 2 * 4 * elems      # read + write per launch
+    fgbs = fb / (fwd_ms * 1e-3) / 1e9
+    bgbs = bb / (bwd_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "RoPE prologue HBM throughput (rotate q or k, bf16)",
+        "value": round(fgbs, 1), "unit": "GB/s", "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_launch": round(fwd_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "s2a_rope_kernel",
+                     "achieved": round(fgbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(fgbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": fb},
+        "bwd": {"ms_per_launch": round(bwd_ms, 4), "bytes_per_launch": bb,
+                "achieved_gbs": round(bgbs, 1),
+                "frac": round(bgbs / PEAK_HBM_GBS, 4)},
+        "config": {"workload": f"RoPE at global positions, B={B} N={N} "
+                               f"H={H} D={D}, half pairing, base 1e4",
+                   "dtype": "bf16 (fwd), f32 (bwd)"},
+    }), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -182,6 +246,9 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.rope:
+        rope_bench(args)
         return
 
     import torch
