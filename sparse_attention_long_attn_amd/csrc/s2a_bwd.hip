@@ -837,6 +837,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = BQ * T::ROWB;
   constexpr int NG2L = 2 * LD::IPW;  // direct loads per wave per tile
+  // (with NBUF >= 4 the wait below would also have to cover stats loads
+  // issued between older tiles' loads)
+  static_assert(NBUF == 2 || NBUF == 3, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * TILEB];
   __shared__ __attribute__((aligned(16))) float lse2s[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) float dlts[NBUF * BQ];
@@ -1119,8 +1122,12 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       dkmfma(1, st);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The next iteration reads tile it + 1, issued NBUF - 2 iterations
+    // before this one's tile; stats(pre) were issued just before this
+    // iteration's tile.  So every load but the tile loads of the last
+    // NBUF - 2 iterations must have landed (vmcnt counts in order).
     if (pre < nq) {
-      wait_vm<NG2L>();  // all but this iteration's tile loads have landed
+      wait_vm<(NBUF - 2) * NG2L>();
       stage_stats(pre % NBUF);
     } else {
       wait_vm_all();
