@@ -234,7 +234,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       if (qsl < glen) {
         const int qp = run.pos(qsl);
         if (qp < L) {
-          l2st = lse[lrow + qp] * S2A_LOG2E;
+          l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
       }
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       *(u32x4 *)(dOs + buf * QT + r * KP + ch * 8) = gst[i];
     }
     if (tid < KV_BQ) {
-      lse2s[buf * KV_BQ + tid] = l2st;
+      lse2s[buf * KV_BQ + tid] = l2st * S2A_LOG2E;
       dlts[buf * KV_BQ + tid] = dlst;
       if (DOC) {
         qdocs[buf * KV_BQ + tid] = qdst;
@@ -825,7 +825,13 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 // The first iterations (the only ones whose queries can precede the
 // workgroup's keys) run a masked copy of the body; the steady state has no
 // mask at all.
-template <int D, int BQ, int NBUF, bool DOC>
+//
+// The two tile buffers are separate LDS variables and every copy of the
+// body names its buffer at compile time.  The compiler can then tell that
+// a body's LDS reads do not touch the buffer its direct loads are filling;
+// with one array and a computed buffer it waited for those loads (the next
+// tile) before the first read, which serialised load and compute.
+template <int D, int BQ, bool DOC>
 __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -836,16 +842,24 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   constexpr int NQB = BQ / 32;  // 32-query blocks per tile
   constexpr int KSTEPS = D / 16, DB = D / 32;
   constexpr int TILEB = BQ * T::ROWB;
-  constexpr int NG2L = 2 * LD::IPW;  // direct loads per wave per tile
-  // (with NBUF >= 4 the wait below would also have to cover stats loads
-  // issued between older tiles' loads)
-  static_assert(NBUF == 2 || NBUF == 3, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * TILEB];
+  constexpr int NBUF = 2;
+  __shared__ __attribute__((aligned(1024))) char Qs0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Qs1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char dOs0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char dOs1[TILEB];
   __shared__ __attribute__((aligned(16))) float lse2s[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) float dlts[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) int qdocs[NBUF * BQ];  // DOC only
-  char *const Qs = smem;
-  char *const dOs = smem + NBUF * TILEB;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  auto qbuf = [&](auto b) -> char * {
+    if constexpr (decltype(b)::value == 0) return Qs0;
+    else return Qs1;
+  };
+  auto gbuf = [&](auto b) -> char * {
+    if constexpr (decltype(b)::value == 0) return dOs0;
+    else return dOs1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -904,7 +918,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       if (qsl < glen) {
         const int qp = run.pos(qsl);
         if (qp < L) {
-          l2st = lse[lrow + qp] * S2A_LOG2E;
+          l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
       }
@@ -912,13 +926,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   };
   auto stage_stats = [&](int buf) {
     if (tid < BQ) {
-      lse2s[buf * BQ + tid] = l2st;
+      lse2s[buf * BQ + tid] = l2st * S2A_LOG2E;
       dlts[buf * BQ + tid] = dlst;
       if (DOC) qdocs[buf * BQ + tid] = qdst;
     }
   };
-  auto issue_tile = [&](int q0, int buf) {
-    char *qd = Qs + buf * TILEB, *gd = dOs + buf * TILEB;
+  auto issue_tile = [&](int q0, auto b) {
+    char *qd = qbuf(b), *gd = gbuf(b);
     if (tile_plain(run, glen, q0, BQ, L)) {
       const size_t r0 = (size_t)run.pos(q0) * rs;
       ld.fast_s(qbh + r0, qd);
@@ -949,14 +963,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     }
 
   const int nq = (glen - k0 + BQ - 1) / BQ;
-#pragma unroll
-  for (int s0 = 0; s0 < NBUF - 1; ++s0)
-    if (s0 < nq) {
-      fetch_stats(k0 + s0 * BQ);
-      wait_vm_all();
-      stage_stats(s0);
-      issue_tile(k0 + s0 * BQ, s0);
-    }
+  fetch_stats(k0);
+  wait_vm_all();
+  stage_stats(0);
+  issue_tile(k0, B0{});
   wait_vm_all();
   __syncthreads();
 
@@ -976,17 +986,19 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       }
     return m;
   };
-  auto body = [&](auto masked_tag, int it) {
+  // body(masked, b, it): iteration it, whose tile sits in buffer b (= it % 2)
+  auto body = [&](auto masked_tag, auto b, int it) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int buf = decltype(b)::value;
+    using BN = std::integral_constant<int, 1 - buf>;
     const int q0 = k0 + it * BQ;
-    const int buf = it % NBUF;
-    const int pre = it + NBUF - 1;  // tile loaded during this iteration
+    const int pre = it + 1;  // tile loaded during this iteration
     if (pre < nq) {
-      fetch_stats(k0 + pre * BQ);   // issued before the tile: waited first
-      issue_tile(k0 + pre * BQ, pre % NBUF);
+      fetch_stats(k0 + pre * BQ);
+      issue_tile(k0 + pre * BQ, BN{});
     }
-    const char *Qb = Qs + buf * TILEB;
-    const char *dOb = dOs + buf * TILEB;
+    const char *Qb = qbuf(b);
+    const char *dOb = gbuf(b);
     const float *l2b = lse2s + buf * BQ;
     const float *dlb = dlts + buf * BQ;
     static_assert(NQB == 2, "the pipeline below is written for two blocks");
@@ -1122,24 +1134,21 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       dkmfma(1, st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // The next iteration reads tile it + 1, issued NBUF - 2 iterations
-    // before this one's tile; stats(pre) were issued just before this
-    // iteration's tile.  So every load but the tile loads of the last
-    // NBUF - 2 iterations must have landed (vmcnt counts in order).
-    if (pre < nq) {
-      wait_vm<(NBUF - 2) * NG2L>();
-      stage_stats(pre % NBUF);
-    } else {
-      wait_vm_all();
-    }
+    // the next iteration reads tile it + 1 and its stats, both issued at
+    // the top of this one
+    wait_vm_all();
+    if (pre < nq) stage_stats(1 - buf);
     __syncthreads();
   };
 
   // Iterations whose queries can precede some of the workgroup's keys.
-  const int npeel = min(nq, (KV_BK + BQ - 1) / BQ);
-  int it = 0;
-  for (; it < npeel; ++it) body(std::true_type{}, it);
-  for (; it < nq; ++it) body(std::false_type{}, it);
+  static_assert((KV_BK + BQ - 1) / BQ == 2, "two masked iterations");
+  body(std::true_type{}, B0{}, 0);
+  if (nq > 1) body(std::true_type{}, B1{}, 1);
+  for (int it = 2; it < nq; it += 2) {
+    body(std::false_type{}, B0{}, it);
+    if (it + 1 < nq) body(std::false_type{}, B1{}, it + 1);
+  }
 
   mfma_agpr_drain();
   if (kin) {
@@ -1400,7 +1409,7 @@ hipError_t launch_dkdv_d(const void *q, const void *k, const void *v,
                   (void *)&p};
   const void *fn;
   if constexpr (D >= 64)
-    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, 2, DOC>;
+    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, DOC>;
   else
     fn = (const void *)s2a_bwd_dkdv_kernel<D, DOC>;
   hipError_t e = hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
