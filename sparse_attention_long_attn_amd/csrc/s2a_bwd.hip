@@ -926,8 +926,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   };
   auto stage_stats = [&](int buf) {
     if (tid < BQ) {
-      lse2s[buf * BQ + tid] = l2st * S2A_LOG2E;
-      dlts[buf * BQ + tid] = dlst;
+      // the initial S and dP accumulators of the row (see the body)
+      lse2s[buf * BQ + tid] = -l2st / p.scale;
+      dlts[buf * BQ + tid] = -dlst;
       if (DOC) qdocs[buf * BQ + tid] = qdst;
     }
   };
@@ -1014,21 +1015,30 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // block; keys outside the group need no mask (their garbage stays in
     // their own dK/dV column, written as zero at the end).
     constexpr int PIPE = 3;
-    f32x4 l2v[2][4], dlv[2][4];
+    const unsigned dmask = DOC ? same_doc_mask(buf) : 0u;
+    // The row statistics enter as the accumulators' initial values:
+    // S starts at -lse/scale and dP at -delta, so after the MFMAs
+    // S = q.k - lse/scale and dP = dO.v - delta, and the element work is
+    // P = exp2(c2 S) (c2 = scale log2 e), dS = P dP.  No register holds
+    // the statistics and no subtraction is left.
+    f32x16 S[2], dP[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        l2v[qb][i4] = *(const f32x4 *)(l2b + 32 * qb + 8 * i4 + 4 * hf);
-        dlv[qb][i4] = *(const f32x4 *)(dlb + 32 * qb + 8 * i4 + 4 * hf);
+        const f32x4 a = *(const f32x4 *)(l2b + 32 * qb + 8 * i4 + 4 * hf);
+        const f32x4 d = *(const f32x4 *)(dlb + 32 * qb + 8 * i4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          S[qb][4 * i4 + e] = a[e];
+          dP[qb][4 * i4 + e] = d[e];
+        }
       }
-    const unsigned dmask = DOC ? same_doc_mask(buf) : 0u;
-    f32x16 S[2], dP[2];
     bf16x8 pb[2][2], sb[2][2];
-    // element work of block qb: P = exp2(S c - lse2), dS = P (dP - delta)
+    // element work of block qb: P = exp2(c2 S), dS = P dP
     auto elem = [&](int qb, int i) {
-      float pp = __builtin_amdgcn_exp2f(fmaf(S[qb][i], c2, -l2v[qb][i >> 2][i & 3]));
-      float ds = pp * (dP[qb][i] - dlv[qb][i >> 2][i & 3]);
+      float pp = __builtin_amdgcn_exp2f(S[qb][i] * c2);
+      float ds = pp * dP[qb][i];
       if (MASKED) {
         const int d0 = q0 + 32 * qb + 4 * hf - key;  // query - key
         if (d0 + 8 * (i >> 2) + (i & 3) < 0) {
@@ -1078,14 +1088,6 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       mfma32_agpr(dvacc[db], tg[qb][st], pb[qb][h2]);
       mfma32_agpr(dkacc[db], tq[qb][st], sb[qb][h2]);
     };
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        S[qb][i] = 0.f;
-        dP[qb][i] = 0.f;
-      }
-
     // P1
 #pragma unroll
     for (int t = 0; t < PIPE; ++t) spload(0, t);
@@ -1281,14 +1283,15 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
     }
     if (tid < KV_BQ) {
       const int s = q0 + tid;
-      float l2 = INFINITY, dl = 0.f;
+      // initial S and dP accumulators, as in s2a_bwd_dkdv_sw_kernel
+      float l2 = -INFINITY, dl = 0.f;
       int dd = 0;
       if (s < glen) {
         const int qp = run.pos(s);
         if (DOC) dd = dbase[qp];
         if (qp < L) {
-          l2 = lse[lrow + qp] * S2A_LOG2E;
-          dl = delta[lrow + qp];
+          l2 = -lse[lrow + qp] / p.scale;
+          dl = -delta[lrow + qp];
         }
       }
       lse2s[tid] = l2;
@@ -1302,9 +1305,14 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 S, dP;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          S[i] = 0.f;
-          dP[i] = 0.f;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l2 = *(const f32x4 *)(lse2s + 32 * qb + 8 * i4 + 4 * hf);
+          const f32x4 dl = *(const f32x4 *)(dlts + 32 * qb + 8 * i4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S[4 * i4 + e] = l2[e];
+            dP[4 * i4 + e] = dl[e];
+          }
         }
 #pragma unroll
         for (int t = 0; t < Dm::KSTEPS; ++t) {
@@ -1318,14 +1326,12 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = 32 * qb + 8 * i4 + 4 * hf;
-          const f32x4 l2 = *(const f32x4 *)(lse2s + r0);
-          const f32x4 dl = *(const f32x4 *)(dlts + r0);
           const i32x4 qd = *(const i32x4 *)(qdocs + r0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            const float pp = __builtin_amdgcn_exp2f(fmaf(S[i], c2, -l2[e]));
-            const float ds = pp * (dP[i] - dl[e]);
+            const float pp = __builtin_amdgcn_exp2f(S[i] * c2);
+            const float ds = pp * dP[i];
             bool ok = kvalid & (key <= q0 + r0 + e);
             if (DOC) ok &= qd[e] == kdoc;
             const float pm = ok ? pp : 0.f, dm = ok ? ds : 0.f;
