@@ -723,79 +723,92 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
     if (k0 <= wq_hi) {
       const char *Kb = Ks + buf * TILEB;
       const char *Vb = Vs + buf * TILEB;
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 ak[KSTEPS], av[KSTEPS];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          ak[t] = *(const bf16x8 *)(Kb + kb * 32 * T::ROWB + aoff[t]);
-          av[t] = *(const bf16x8 *)(Vb + kb * 32 * T::ROWB + aoff[t]);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[kb][i] = 0.f;
-          dpacc[kb][i] = 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-          sacc[kb] = mfma32(ak[t], qreg[t], sacc[kb]);
-          dpacc[kb] = mfma32(av[t], greg[t], dpacc[kb]);
-        }
-      }
       const bool diag = (k0 + DQ_BK - 1 > wq_lo) ||
                         !tile_plain(run, glen, k0, DQ_BK, L);
       const bool edge = DOC || diag;
       const bool resid = diag || (wave_hot && k0 + 2 * DQ_BK - 2 >= wq_lo);
+      // One 32-key block at a time (fewer live accumulators, so the
+      // compiler can keep operand reads ahead of the MFMAs).
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc, dpacc;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          i32x4 kd = {0, 0, 0, 0};
-          if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+        for (int i = 0; i < 16; ++i) {
+          sacc[i] = 0.f;
+          dpacc[i] = 0.f;
+        }
+        // operand reads run PIPE steps ahead of their MFMAs (the fences
+        // keep the compiler from waiting on each read just before its use)
+        constexpr int PIPE = 3;
+        bf16x8 ak[KSTEPS], av[KSTEPS];
+        auto opload = [&](int t) {
+          ak[t] = *(const bf16x8 *)(Kb + kb * 32 * T::ROWB + aoff[t]);
+          av[t] = *(const bf16x8 *)(Vb + kb * 32 * T::ROWB + aoff[t]);
+        };
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * g4 + j;
-            float pp = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c2, -l2));
-            if (edge) {
+        for (int t = 0; t < PIPE; ++t) opload(t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          if (t + PIPE < KSTEPS) opload(t + PIPE);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc = mfma32(ak[t], qreg[t], sacc);
+          dpacc = mfma32(av[t], greg[t], dpacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // mask where the tile crosses the diagonal, the group end,
+        // padding, or (under a document mask) anywhere
+        if (edge) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            i32x4 kd = {0, 0, 0, 0};
+            if (DOC) kd = *(const i32x4 *)&kdoc[buf][32 * kb + 8 * g4 + 4 * hf];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * g4 + j;
               const int ks = k0 + 32 * kb + 8 * g4 + 4 * hf + j;
               bool ok = (ks <= qslot) & (ks < glen) & (run.pos(ks) < L);
               if (DOC) ok &= kd[j] == qdoc;
-              pp = ok ? pp : 0.f;
+              sacc[i] = ok ? sacc[i] : -INFINITY;
             }
-            dpacc[kb][i] = pp * (dpacc[kb][i] - dl);
           }
         }
-      // dQ^T += K^T dS^T.  On diagonal tiles (where rows see few keys and
-      // |dS| is largest), tiles with padding or the group end, and the
-      // tiles of hot queries, dS goes in as bf16 hi + lo parts, which
-      // removes most of the bf16 rounding of dS from those rows' error.
-      // pass 0: dS rounded to bf16; pass 1 (those tiles only): the
-      // rounding residual dS - bf16(dS), also in bf16
-      auto dq_product = [&](auto lo_tag) {
-        constexpr bool LO = decltype(lo_tag)::value;
 #pragma unroll
-        for (int ks = 0; ks < DQ_BK / 16; ++ks) {
-          const f32x16 &dp = dpacc[ks >> 1];
-          const int e0 = 8 * (ks & 1);
-          bf16x8 sb = to_bf16x8(dp[e0], dp[e0 + 1], dp[e0 + 2], dp[e0 + 3],
-                                dp[e0 + 4], dp[e0 + 5], dp[e0 + 6], dp[e0 + 7]);
-          if constexpr (LO)
-            sb = to_bf16x8(dp[e0] - (float)sb[0], dp[e0 + 1] - (float)sb[1],
-                           dp[e0 + 2] - (float)sb[2], dp[e0 + 3] - (float)sb[3],
-                           dp[e0 + 4] - (float)sb[4], dp[e0 + 5] - (float)sb[5],
-                           dp[e0 + 6] - (float)sb[6], dp[e0 + 7] - (float)sb[7]);
-          const char *kr = Kb + 16 * ks * T::ROWB;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[db])),
-                                   lds_read_tr((const bf16_t *)(kr + troff8[db])));
-            dqacc[db] = mfma32(ak, sb, dqacc[db]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const float pp = __builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -l2));
+          dpacc[i] = pp * (dpacc[i] - dl);
         }
-      };
-      dq_product(std::false_type{});
-      if (resid) dq_product(std::true_type{});
+        // dQ^T += K^T dS^T over the block's 32 keys.  On diagonal tiles
+        // (where rows see few keys and |dS| is largest), tiles with padding
+        // or the group end, and the tiles of hot queries, dS goes in as
+        // bf16 hi + lo parts, which removes most of the bf16 rounding of dS
+        // from those rows' error.  pass 0: dS rounded to bf16; pass 1 (those
+        // tiles only): the rounding residual dS - bf16(dS), also in bf16
+        auto dq_product = [&](auto lo_tag) {
+          constexpr bool LO = decltype(lo_tag)::value;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e0 = 8 * h;
+            bf16x8 sb = to_bf16x8(dpacc[e0], dpacc[e0 + 1], dpacc[e0 + 2],
+                                  dpacc[e0 + 3], dpacc[e0 + 4], dpacc[e0 + 5],
+                                  dpacc[e0 + 6], dpacc[e0 + 7]);
+            if constexpr (LO)
+              sb = to_bf16x8(dpacc[e0] - (float)sb[0], dpacc[e0 + 1] - (float)sb[1],
+                             dpacc[e0 + 2] - (float)sb[2], dpacc[e0 + 3] - (float)sb[3],
+                             dpacc[e0 + 4] - (float)sb[4], dpacc[e0 + 5] - (float)sb[5],
+                             dpacc[e0 + 6] - (float)sb[6], dpacc[e0 + 7] - (float)sb[7]);
+            const char *kr = Kb + (32 * kb + 16 * h) * T::ROWB;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[db])),
+                                     lds_read_tr((const bf16_t *)(kr + troff8[db])));
+              dqacc[db] = mfma32(ak, sb, dqacc[db]);
+            }
+          }
+        };
+        dq_product(std::false_type{});
+        if (resid) dq_product(std::true_type{});
+      }
     }
     wait_vm_all();
     __syncthreads();
