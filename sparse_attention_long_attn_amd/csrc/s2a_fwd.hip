@@ -417,17 +417,30 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     if (k0 <= wq_hi) {
       const char *Kb = Ks + buf * TILEB;
       const char *Vb = Vs + buf * TILEB;
+      // S^T = K Q^T, 16 MFMAs over (kb, t); each operand read runs PIPE
+      // steps ahead of its MFMA (the fences keep the compiler from waiting
+      // on every read right before its use)
       f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 a[KSTEPS];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
-          a[t] = *(const bf16x8 *)(Kb + kb * 32 * T::ROWB + koff[t]);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      constexpr int PIPE = 3, NS = 2 * KSTEPS;
+      bf16x8 a[NS];
+      auto opload = [&](int st) {
+        a[st] = *(const bf16x8 *)(Kb + (st / KSTEPS) * 32 * T::ROWB +
+                                  koff[st % KSTEPS]);
+      };
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) sacc[kb] = mfma32(a[t], qreg[t], sacc[kb]);
+      for (int st = 0; st < PIPE; ++st) opload(st);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        if (st + PIPE < NS) opload(st + PIPE);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = st / KSTEPS, t = st % KSTEPS;
+        sacc[kb] = mfma32(a[st], qreg[t], sacc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       const bool edge = DOC || (k0 + FWD_BK - 1 > wq_lo) ||

@@ -16,6 +16,8 @@
 // each; the xor keeps a chunk pair together) at ~122 B/clk per CU.  An
 // unpermuted layout gets 16 and 64 B/clk respectively.
 #pragma once
+#include <stdint.h>
+
 #include "s2a_device.h"
 
 template <int D>
@@ -33,16 +35,42 @@ struct SwTile {
 
 // Direct global -> LDS copy of 16 bytes per lane.  lds_wave must be the
 // same for every lane of the wave (it is kept in M0).
+//
+// Written as inline asm on purpose: the compiler counts these loads as
+// outstanding LDS operations too, and then waits for every LDS read in
+// flight (lgkmcnt(0)) wherever a read result is used, instead of only for
+// the oldest.  Hidden from it, the loads are waited for explicitly: every
+// kernel ends each tile with s_waitcnt vmcnt(0) and a barrier before the
+// buffer is read.  No VGPR is written (the data goes to LDS), and "memory"
+// keeps the loads in program order with the barriers and LDS accesses.
 __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave) {
-  __builtin_amdgcn_global_load_lds(
-      gptr, (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
+  const unsigned m0 = (unsigned)(uintptr_t)lds_wave;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(m0)
+               : "memory", "m0");
+}
+
+// The same with a wave-uniform base address and a 32-bit per-lane byte
+// offset (the scalar-base form of the instruction).
+__device__ __forceinline__ void g2lds16_s(const void *gbase, unsigned off,
+                                          void *lds_wave) {
+  const unsigned m0 = (unsigned)(uintptr_t)lds_wave;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(gbase), "s"(m0)
+               : "memory", "m0");
 }
 
 // Direct global -> LDS copy of 4 bytes per lane (lane i lands at byte 4*i
-// past lds_wave, which must be the same for every lane of the wave).
+// past lds_wave, which must be the same for every lane of the wave).  Inline
+// asm for the reason given at g2lds16.
 __device__ __forceinline__ void g2lds4(const void *gptr, void *lds_wave) {
-  __builtin_amdgcn_global_load_lds(
-      gptr, (__attribute__((address_space(3))) void *)lds_wave, 4, 0, 0);
+  const unsigned m0 = (unsigned)(uintptr_t)lds_wave;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(m0)
+               : "memory", "m0");
 }
 
 // Loader of one ROWS-row tile of a [B,N,H,D] tensor by NWAVES waves.  Each
@@ -86,8 +114,7 @@ struct TileLoader {
   // addresses stay live across a loop.
   __device__ void fast_s(const bf16_t *g0, char *lds) const {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      g2lds16((const char *)g0 + boff[i], lds + ldsb[i]);
+    for (int i = 0; i < IPW; ++i) g2lds16_s(g0, boff[i], lds + ldsb[i]);
   }
 
   // General rows: slot s0 + row of the group (run, glen); rows outside
