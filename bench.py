@@ -50,6 +50,11 @@ def parse():
                          "prologue (rotate q and k, bf16) and its gradient "
                          "map (dq and dk, fp32, in place) at the headline "
                          "shape (one JSON line, HBM roofline)")
+    ap.add_argument("--docs", type=int, default=0, metavar="MEAN_LEN",
+                    help="instead of the headline line, time the headline "
+                         "step under a document mask of packed samples with "
+                         "geometric lengths of this mean (one JSON line; "
+                         "useful work counts only same-document pairs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a plain copy "
                          "kernel of known size, to calibrate HBM counters)")
@@ -235,6 +240,66 @@ def rope_bench(args):
     }), flush=True)
 
 
+def docs_bench(args):
+    """The headline step (forward, preprocess, dK/dV, dQ) under a document
+    mask: packed samples of geometric length with the given mean.  Useful
+    FLOPs are 14*D per allowed same-document pair; tiles whose document IDs
+    cannot meet are skipped by the kernels."""
+    import torch
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    from sparse_attention_long_attn_amd import work
+    cfg = WORKLOAD
+    B, N, H, D, G, L, bnd = (cfg[k] for k in ("B", "N", "H", "D", "G", "L",
+                                              "boundary"))
+    shift = G // 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ins = syn.make_inputs(cfg["config"], 0, B, N, H, D, with_do=True, L=L)
+    q, k, v, do = (torch.from_numpy(ins[t].view("int16")).view(torch.bfloat16)
+                   .to(dev) for t in ("q", "k", "v", "do"))
+    del ins
+    doc = syn.make_doc_ids(7000 + args.docs, B, N, args.docs)
+    dd = torch.from_numpy(doc).to(dev)
+    o = torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+                  for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    kw = dict(G=G, shift=shift, boundary=bnd, valid_len=L, doc_ids=dd)
+
+    def step():
+        s2a.fwd(q, k, v, o=o, lse=lse, **kw)
+        s2a.bwd_preprocess(o, do, delta)
+        s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
+        s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = work.total_doc_pairs(B, N, H, G, shift, bnd, L, doc)
+    dense = work.total_pairs(B, N, H, G, shift, bnd, L)
+    useful = 14 * D * pairs
+    print(json.dumps({
+        "metric": "S2-Attn fwd+bwd useful TFLOP/s under a document mask",
+        "value": round(useful / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "higher_is_better": True, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": f"B={B} N={N} H={H} D={D} G={G} wrap, packed "
+                               f"documents of mean length {args.docs}",
+                   "documents": int(doc.max()) + 1, "allowed_pairs": pairs,
+                   "fraction_of_unmasked_pairs": round(pairs / dense, 4)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -249,6 +314,9 @@ def main():
         return
     if args.rope:
         rope_bench(args)
+        return
+    if args.docs:
+        docs_bench(args)
         return
 
     import torch

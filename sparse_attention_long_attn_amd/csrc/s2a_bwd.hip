@@ -619,6 +619,8 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   constexpr int TILEB = DQ_BK * T::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
   __shared__ __attribute__((aligned(16))) int kdoc[2][DQ_BK];  // DOC only
+  __shared__ unsigned klive[DOC_WORDS];                        // DOC only
+  __shared__ int rng[2 * (DQ_THREADS / 64)];                   // DOC only
   char *const Ks = smem;
   char *const Vs = smem + 2 * TILEB;
 
@@ -650,6 +652,9 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   const int qdoc = DOC ? p.doc[(size_t)ut.b * N + qpos] : 0;
   // a hot query (see HOT_SPAN) reads keys of at most two key tiles: the
   // diagonal one and the one before it
+  // Document IDs the wave's queries span (see the forward kernel).
+  int qdmn = qvalid ? qdoc : INT_MAX, qdmx = qvalid ? qdoc : INT_MIN;
+  if (DOC) wave_minmax(qdmn, qdmx);
   const bool wave_hot =
       DOC && __any(qin && p.doc[(size_t)ut.b * N +
                                 run.pos(qslot >= HOT_SPAN ? qslot - HOT_SPAN : 0)] != qdoc);
@@ -710,22 +715,40 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   const int wq_lo = q0 + 32 * w;
   const int wq_hi = wq_lo + 31;
 
-  issue(0, 0);
+  // Under a document mask only the key tiles whose IDs can meet the
+  // workgroup's queries' are walked.
+  if (DOC) {
+    int mn = qdmn, mx = qdmx;
+    wg_range<DQ_THREADS / 64>(mn, mx, rng, w, lane);
+    doc_tiles<DQ_THREADS / 64>(p.doc + (size_t)ut.b * N, run, glen, L, 0,
+                               ntiles, mn, mx, 0, klive, nullptr, w, lane);
+  }
+  int it = DOC ? next_tile(klive, 0, ntiles) : 0;
+  if (it < ntiles) issue(it * DQ_BK, 0);
   wait_vm_all();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int buf = 0; it < ntiles; buf ^= 1) {
     const int k0 = it * DQ_BK;
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) issue(k0 + DQ_BK, buf ^ 1);
+    const int nx = DOC ? next_tile(klive, it + 1, ntiles) : it + 1;
+    const bool more = nx < ntiles;
+    if (more) issue(nx * DQ_BK, buf ^ 1);
 
-    if (k0 <= wq_hi) {
+    // (docedge: the tile's keys and the wave's queries are not all of one
+    // document, so the document mask must be applied)
+    bool live = k0 <= wq_hi, docedge = false;
+    if (DOC && live) {
+      int kmn = kdoc[buf][lane], kmx = kmn;
+      wave_minmax(kmn, kmx);
+      live = kmx >= qdmn && kmn <= qdmx;
+      docedge = !(kmn == kmx && qdmn == qdmx && kmn == qdmn);
+    }
+    if (live) {
       const char *Kb = Ks + buf * TILEB;
       const char *Vb = Vs + buf * TILEB;
       const bool diag = (k0 + DQ_BK - 1 > wq_lo) ||
                         !tile_plain(run, glen, k0, DQ_BK, L);
-      const bool edge = DOC || diag;
+      const bool edge = docedge || diag;
       const bool resid = diag || (wave_hot && k0 + 2 * DQ_BK - 2 >= wq_lo);
       // One 32-key block at a time (fewer live accumulators, so the
       // compiler can keep operand reads ahead of the MFMAs).
@@ -812,6 +835,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
     }
     wait_vm_all();
     __syncthreads();
+    it = nx;
   }
 
   if (qin) {
@@ -863,6 +887,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   __shared__ __attribute__((aligned(16))) float lse2s[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) float dlts[NBUF * BQ];
   __shared__ __attribute__((aligned(16))) int qdocs[NBUF * BQ];  // DOC only
+  __shared__ unsigned qlive[DOC_WORDS];                           // DOC only
+  __shared__ int rng[2 * (THREADS / 64)];                         // DOC only
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   auto qbuf = [&](auto b) -> char * {
@@ -899,6 +925,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
   const int kdoc = DOC ? p.doc[(size_t)ut.b * N + kpos] : 0;
+  // Document IDs the wave's keys span: a query tile whose IDs all lie
+  // outside [kdmn, kdmx] shares no document with them and is skipped.
+  int kdmn = kvalid ? kdoc : INT_MAX, kdmx = kvalid ? kdoc : INT_MIN;
+  if (DOC) wave_minmax(kdmn, kdmx);
 
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
   {
@@ -977,10 +1007,20 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     }
 
   const int nq = (glen - k0 + BQ - 1) / BQ;
-  fetch_stats(k0);
-  wait_vm_all();
-  stage_stats(0);
-  issue_tile(k0, B0{});
+  // Under a document mask only the query tiles whose IDs can meet the
+  // workgroup's keys' are walked.
+  if (DOC) {
+    int mn = kdmn, mx = kdmx;
+    wg_range<THREADS / 64>(mn, mx, rng, w, lane);
+    doc_tiles<THREADS / 64>(p.doc + (size_t)ut.b * N, run, glen, L, k0, nq,
+                            mn, mx, 0, qlive, nullptr, w, lane);
+  }
+  if (!DOC || tile_bit(qlive, 0)) {
+    fetch_stats(k0);
+    wait_vm_all();
+    stage_stats(0);
+    issue_tile(k0, B0{});
+  }
   wait_vm_all();
   __syncthreads();
 
@@ -1001,13 +1041,17 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     return m;
   };
   // body(masked, b, it): iteration it, whose tile sits in buffer b (= it % 2)
+  // body(masked, b, it): query tile it, held in buffer b (= it % 2).  Under
+  // a document mask a tile the workgroup does not walk is neither loaded
+  // nor computed: its iteration costs a barrier.
   auto body = [&](auto masked_tag, auto b, int it) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int buf = decltype(b)::value;
     using BN = std::integral_constant<int, 1 - buf>;
     const int q0 = k0 + it * BQ;
     const int pre = it + 1;  // tile loaded during this iteration
-    if (pre < nq) {
+    const bool pre_live = pre < nq && (!DOC || tile_bit(qlive, pre));
+    if (pre_live) {
       fetch_stats(k0 + pre * BQ);
       issue_tile(k0 + pre * BQ, BN{});
     }
@@ -1028,7 +1072,17 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // block; keys outside the group need no mask (their garbage stays in
     // their own dK/dV column, written as zero at the end).
     constexpr int PIPE = 3;
-    const unsigned dmask = DOC ? same_doc_mask(buf) : 0u;
+    bool live = !DOC || tile_bit(qlive, it), single = false;
+    if (DOC && live) {
+      static_assert(BQ == 64, "one query document ID per lane");
+      int qmn = qdocs[buf * BQ + lane], qmx = qmn;
+      wave_minmax(qmn, qmx);
+      live = qmx >= kdmn && qmn <= kdmx;
+      // all of the tile's queries and the wave's keys in one document
+      single = qmn == qmx && kdmn == kdmx && qmn == kdmn;
+    }
+    if (live) {
+    const unsigned dmask = DOC ? (single ? ~0u : same_doc_mask(buf)) : 0u;
     // The row statistics enter as the accumulators' initial values:
     // S starts at -lse/scale and dP at -delta, so after the MFMAs
     // S = q.k - lse/scale and dP = dO.v - delta, and the element work is
@@ -1149,10 +1203,11 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       dkmfma(1, st);
       __builtin_amdgcn_sched_barrier(0);
     }
+    }  // live
     // the next iteration reads tile it + 1 and its stats, both issued at
     // the top of this one
     wait_vm_all();
-    if (pre < nq) stage_stats(1 - buf);
+    if (pre_live) stage_stats(1 - buf);
     __syncthreads();
   };
 
@@ -1210,6 +1265,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
   __shared__ __attribute__((aligned(16))) float lse2s[KV_BQ];
   __shared__ __attribute__((aligned(16))) float dlts[KV_BQ];
   __shared__ __attribute__((aligned(16))) int qdocs[KV_BQ];
+  __shared__ unsigned qlive[DOC_WORDS], qhot[DOC_WORDS];  // DOC only
+  __shared__ int rng[2 * (THREADS / 64)];                 // DOC only
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -1263,17 +1320,24 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
 
   bool any_hot = false;
   const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
+  // Under a document mask: the query tiles that can meet the workgroup's
+  // keys' documents and hold hot queries.
+  if (DOC) {
+    int mn = kvalid ? kdoc : INT_MAX, mx = kvalid ? kdoc : INT_MIN;
+    wg_range<THREADS / 64>(mn, mx, rng, w, lane);
+    doc_tiles<THREADS / 64>(dbase, run, glen, L, k0, nq, mn, mx, HOT_SPAN,
+                            qlive, qhot, w, lane);
+  }
   for (int it = 0; it < nq; ++it) {
     const int q0 = k0 + it * KV_BQ;
     if (!DOC && q0 >= HOT_SPAN) break;
-    // Every wave evaluates the same test, so the branch is uniform across
+    // The test is the same in every wave, so the branch is uniform across
     // the workgroup and the barriers below are reached by all waves.
-    const int qsl = q0 + lane;
-    bool h = qsl < glen && qsl < HOT_SPAN;
-    if (DOC && qsl < glen)
-      h |= dbase[run.pos(qsl)] !=
-           dbase[run.pos(qsl >= HOT_SPAN ? qsl - HOT_SPAN : 0)];
-    if (!__any(h)) continue;
+    if (DOC) {
+      if (!(tile_bit(qlive, it) && tile_bit(qhot, it))) continue;
+    } else {
+      if (!__any(q0 + lane < glen)) continue;  // (tile 0: always hot)
+    }
     any_hot = true;
 
     __syncthreads();  // the previous hot tile's reads are done

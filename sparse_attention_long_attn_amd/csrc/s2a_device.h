@@ -93,6 +93,18 @@ __device__ __forceinline__ float wave_max_x32(float x) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
+// Minimum and maximum of an int over the 64 lanes of a wave, returned
+// wave-uniform.
+__device__ __forceinline__ void wave_minmax(int &mn, int &mx) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, __shfl_xor(mn, o, 64));
+    mx = max(mx, __shfl_xor(mx, o, 64));
+  }
+  mn = __builtin_amdgcn_readfirstlane(mn);
+  mx = __builtin_amdgcn_readfirstlane(mx);
+}
+
 __device__ __forceinline__ float wave_sum_x32(float x) {
   float a = x, b = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));

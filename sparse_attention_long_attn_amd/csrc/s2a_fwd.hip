@@ -309,6 +309,8 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   constexpr int TILEB = FWD_BK * T::ROWB;  // bytes per tile buffer
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
   __shared__ __attribute__((aligned(16))) int kdoc[2][FWD_BK];  // DOC only
+  __shared__ unsigned klive[DOC_WORDS];                          // DOC only
+  __shared__ int rng[2 * (FWD_THREADS / 64)];                    // DOC only
   char *const Ks = smem;              // two K buffers
   char *const Vs = smem + 2 * TILEB;  // two V buffers
 
@@ -341,6 +343,10 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   const int qpos = qin ? run.pos(qslot) : 0;
   const bool qvalid = qin && qpos < L;
   const int qdoc = DOC ? p.doc[(size_t)b * N + qpos] : 0;
+  // Document IDs the wave's valid queries span: a key tile whose IDs all
+  // lie outside [qdmn, qdmx] shares no document with them and is skipped.
+  int qdmn = qvalid ? qdoc : INT_MAX, qdmx = qvalid ? qdoc : INT_MIN;
+  if (DOC) wave_minmax(qdmn, qdmx);
 
   bf16x8 qreg[KSTEPS];
   {
@@ -404,17 +410,35 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   const int wq_hi = wq_lo + 31;
   const float c2 = p.scale_log2;
 
-  issue(0, 0);
+  // Under a document mask the workgroup walks only the key tiles whose IDs
+  // can meet its queries' (the rest would be masked out entirely).
+  if (DOC) {
+    int mn = qdmn, mx = qdmx;
+    wg_range<FWD_THREADS / 64>(mn, mx, rng, w, lane);
+    doc_tiles<FWD_THREADS / 64>(p.doc + (size_t)b * N, run, glen, L, 0,
+                                ntiles, mn, mx, 0, klive, nullptr, w, lane);
+  }
+  int it = DOC ? next_tile(klive, 0, ntiles) : 0;
+  if (it < ntiles) issue(it * FWD_BK, 0);
   wait_vm_all();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int buf = 0; it < ntiles; buf ^= 1) {
     const int k0 = it * FWD_BK;
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) issue(k0 + FWD_BK, buf ^ 1);  // lands during this tile's math
+    const int nx = DOC ? next_tile(klive, it + 1, ntiles) : it + 1;
+    const bool more = nx < ntiles;
+    if (more) issue(nx * FWD_BK, buf ^ 1);  // lands during this tile's math
 
-    if (k0 <= wq_hi) {
+    // (docedge: the tile's keys and the wave's queries are not all of one
+    // document, so the document mask must be applied)
+    bool live = k0 <= wq_hi, docedge = false;
+    if (DOC && live) {
+      int kmn = kdoc[buf][lane], kmx = kmn;
+      wave_minmax(kmn, kmx);
+      live = kmx >= qdmn && kmn <= qdmx;
+      docedge = !(kmn == kmx && qdmn == qdmx && kmn == qdmn);
+    }
+    if (live) {
       const char *Kb = Ks + buf * TILEB;
       const char *Vb = Vs + buf * TILEB;
       // S^T = K Q^T, 16 MFMAs over (kb, t); each operand read runs PIPE
@@ -443,7 +467,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      const bool edge = DOC || (k0 + FWD_BK - 1 > wq_lo) ||
+      const bool edge = docedge || (k0 + FWD_BK - 1 > wq_lo) ||
                         !tile_plain(run, glen, k0, FWD_BK, L);
       if (edge) {
 #pragma unroll
@@ -511,6 +535,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     }
     wait_vm_all();
     __syncthreads();
+    it = nx;
   }
 
   const float lt = wave_sum_x32(l_run);

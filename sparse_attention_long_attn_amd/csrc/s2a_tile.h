@@ -16,6 +16,7 @@
 // each; the xor keeps a chunk pair together) at ~122 B/clk per CU.  An
 // unpermuted layout gets 16 and 64 B/clk respectively.
 #pragma once
+#include <limits.h>
 #include <stdint.h>
 
 #include "s2a_device.h"
@@ -55,10 +56,17 @@ __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave) {
 // offset (the scalar-base form of the instruction).
 __device__ __forceinline__ void g2lds16_s(const void *gbase, unsigned off,
                                           void *lds_wave) {
-  const unsigned m0 = (unsigned)(uintptr_t)lds_wave;
+  // (both are wave-uniform; readfirstlane tells the compiler so, which the
+  // scalar operands need)
+  const unsigned m0 =
+      (unsigned)__builtin_amdgcn_readfirstlane((int)(uintptr_t)lds_wave);
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint64_t gu =
+      ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
+      (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)g);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(off), "s"(gbase), "s"(m0)
+               : "v"(off), "s"(gu), "s"(m0)
                : "memory", "m0");
 }
 
@@ -159,4 +167,123 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) |
                              (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Document-mask tile lists.  A kernel that walks the 64-slot tiles
+// t0, t0 + 64, ... of a group needs only the tiles whose document IDs can
+// meet those of its own rows.  doc_tiles() marks, one bit per tile in the
+// LDS words live[], every tile j whose valid slots (inside the group, at a
+// position below L) hold IDs spanning a range that meets [lo, hi]; with
+// hot != nullptr it also marks tiles holding a "hot" slot s: s < span, or
+// an ID different from that of slot s - span (a row that sees few keys).
+// Tiles past DOC_MAXT are all marked live (and hot): correct, not skipped.
+// Every thread of the workgroup calls it; it ends with a barrier.
+constexpr int DOC_MAXT = 1024;            // tiles tracked (groups <= 64K)
+constexpr int DOC_WORDS = DOC_MAXT / 32;
+
+// Bits 0, 2, 4, ... of x packed into bits 0..31.
+__device__ __forceinline__ unsigned even_bits(unsigned long long x) {
+  x &= 0x5555555555555555ull;
+  x = (x | (x >> 1)) & 0x3333333333333333ull;
+  x = (x | (x >> 2)) & 0x0f0f0f0f0f0f0f0full;
+  x = (x | (x >> 4)) & 0x00ff00ff00ff00ffull;
+  x = (x | (x >> 8)) & 0x0000ffff0000ffffull;
+  x = (x | (x >> 16)) & 0x00000000ffffffffull;
+  return (unsigned)x;
+}
+
+template <int NW>
+__device__ void doc_tiles(const int *docb, const S2ARun &run, int glen, int L,
+                          int t0, int ntiles, int lo, int hi, int span,
+                          unsigned *live, unsigned *hot, int w, int lane) {
+  const int nw = (min(ntiles, DOC_MAXT) + 31) / 32;
+  for (int k = w; k < DOC_WORDS; k += NW) {
+    unsigned lbits = ~0u, hbits = ~0u;  // beyond the tracked tiles: walk all
+    if (k < nw) {
+      // Word k covers tiles 32k .. 32k+31; lane l reads the 32 slots of half
+      // l % 2 of tile 32k + l / 2 (all loads of a batch in flight at once).
+      const int sb = t0 + 64 * 32 * k + 32 * lane;
+      int mn = INT_MAX, mx = INT_MIN;
+      bool h = false;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        int d[16], r[16];
+        bool vv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int s = sb + 16 * part + e;
+          bool v = s < glen;
+          const int pos = v ? run.pos(s) : 0;
+          v = v && pos < L;
+          vv[e] = v;
+          d[e] = docb[pos];
+          r[e] = 0;
+          if (hot != nullptr) {
+            const int rs = s >= span ? s - span : 0;
+            r[e] = docb[run.pos(rs < glen ? rs : 0)];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int s = sb + 16 * part + e;
+          if (vv[e]) {
+            mn = min(mn, d[e]);
+            mx = max(mx, d[e]);
+            if (hot != nullptr) h = h || s < span || r[e] != d[e];
+          }
+        }
+      }
+      // the two halves of each tile
+      mn = min(mn, __shfl_xor(mn, 1, 64));
+      mx = max(mx, __shfl_xor(mx, 1, 64));
+      h = h || __shfl_xor((int)h, 1, 64);
+      lbits = even_bits(__ballot(mx >= lo && mn <= hi));
+      hbits = even_bits(__ballot(h));
+    }
+    if (lane == 0) {
+      live[k] = lbits;
+      if (hot != nullptr) hot[k] = hbits;
+    }
+  }
+  __syncthreads();
+}
+
+// First tile >= j whose bit is set in words[] (ntiles if none); tiles past
+// DOC_MAXT count as set.  Wave-uniform.
+__device__ __forceinline__ int next_tile(const unsigned *words, int j,
+                                         int ntiles) {
+  while (j < ntiles && j < DOC_MAXT) {
+    // (every lane reads the same word: made uniform for the compiler)
+    const unsigned b =
+        (unsigned)__builtin_amdgcn_readfirstlane((int)words[j >> 5]) >> (j & 31);
+    if (b) return j + __builtin_ctz(b);
+    j = (j | 31) + 1;
+  }
+  return min(j, ntiles);
+}
+
+// Whether tile j is set in words[] (tiles past DOC_MAXT count as set).
+__device__ __forceinline__ bool tile_bit(const unsigned *words, int j) {
+  if (j >= DOC_MAXT) return true;
+  const unsigned w = (unsigned)__builtin_amdgcn_readfirstlane((int)words[j >> 5]);
+  return (w >> (j & 31)) & 1u;
+}
+
+// [min, max] of (mn, mx) over the workgroup's waves, through 2*NW ints of
+// LDS scratch; every thread gets the result.  Contains barriers.
+template <int NW>
+__device__ void wg_range(int &mn, int &mx, int *scratch, int w, int lane) {
+  wave_minmax(mn, mx);
+  if (lane == 0) {
+    scratch[2 * w] = mn;
+    scratch[2 * w + 1] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mn = min(mn, scratch[2 * i]);
+    mx = max(mx, scratch[2 * i + 1]);
+  }
+  __syncthreads();
 }

@@ -71,3 +71,32 @@ def algorithmic_bytes(B, N, H, D, o_bytes=4):
     fwd = 3 * 2 * e + o_bytes * e + 4 * rows
     bwd = 4 * 2 * e + o_bytes * e + 3 * 4 * e + 3 * 4 * rows
     return fwd, bwd
+
+
+def doc_pairs(N, G, shift, boundary, L, doc_row):
+    """Allowed pairs per head of class 0 and class 1 under a document mask
+    (one batch row's int [N] document IDs): inside a group a valid query
+    reads every earlier-or-equal valid slot with its own ID, so a label that
+    occurs n times among a group's valid members contributes n(n+1)/2."""
+    import numpy as np
+    doc_row = np.asarray(doc_row)
+    out = []
+    for cls in (0, 1):
+        tot = 0
+        for runs in _groups(N, G, shift, boundary, cls):
+            ids = np.concatenate([doc_row[a:min(b, L)] for a, b in runs
+                                  if min(b, L) > a] or [np.zeros(0, int)])
+            if ids.size:
+                _, n = np.unique(ids, return_counts=True)
+                tot += int(np.sum(n * (n + 1) // 2))
+        out.append(tot)
+    return tuple(out)
+
+
+def total_doc_pairs(B, N, H, G, shift, boundary, L, doc):
+    """Allowed pairs of the whole batch under document IDs doc [B, N]."""
+    tot = 0
+    for b in range(B):
+        c0, c1 = doc_pairs(N, G, shift, boundary, L, doc[b])
+        tot += (H // 2) * (c0 + c1)
+    return tot

@@ -142,6 +142,29 @@ def test_work_pairs_match_oracle_enumeration(N, G, L, boundary, half):
         oracle.allowed_pairs(N, G, shift, boundary, L)
 
 
+@pytest.mark.parametrize("N,G,L,mean", [(64, 16, 64, 5), (64, 16, 50, 20),
+                                        (96, 32, 81, 7), (256, 64, 250, 40),
+                                        (128, 128, 100, 300)])
+@pytest.mark.parametrize("boundary", [0, 1, 2])
+@pytest.mark.parametrize("half", [0, 1])
+def test_work_doc_pairs_match_oracle_enumeration(N, G, L, mean, boundary,
+                                                 half):
+    import numpy as np
+    import synthetic as syn
+    from oracle.s2attn_oracle import _with_docs
+    shift = half * G // 2
+    doc = syn.make_doc_ids(N + G + mean, 1, N, mean, cuts=(G // 3, G))
+    rows = np.arange(N)
+    want = tuple(int(_with_docs(oracle.adjacency_block(c, rows, N, G, shift,
+                                                       boundary, L),
+                                doc, 0, rows, np.arange(N)).sum())
+                 for c in (0, 1))
+    assert work.doc_pairs(N, G, shift, boundary, L, doc[0]) == want
+    one = np.zeros(N, np.int32)
+    assert work.doc_pairs(N, G, shift, boundary, L, one) == \
+        work.allowed_pairs(N, G, shift, boundary, L)
+
+
 def test_work_pairs_of_the_headline_workload():
     # N=32768, G=8192, WRAP: both classes M*G*(G+1)/2
     c0, c1 = work.allowed_pairs(32768, 8192, 4096, 0, 32768)
