@@ -45,9 +45,10 @@ def gen(config, variant, B, N, H, D, L, heads, with_do):
     return dev, host
 
 
-def sample_rows(N, G, shift, boundary, L, cls):
+def sample_rows(N, G, shift, boundary, L, cls, doc=None):
     """{group index: (query positions, tail positions)} for the groups
-    sampled in head class ``cls``."""
+    sampled in head class ``cls`` (with document IDs, also around the first
+    document starts inside each sampled group)."""
     segs = oracle.segments(N, G, shift, boundary)[cls]
     picks = sorted({0, len(segs) // 2, len(segs) - 1})
     out = {}
@@ -62,25 +63,32 @@ def sample_rows(N, G, shift, boundary, L, cls):
                 slots |= set(range(max(0, j - R // 2), min(n, j + R // 2)))
         if s and cls == 1 and boundary != syn.SPLIT and g == len(segs) - 1:
             slots |= set(range(max(0, s - R // 2), min(n, s + R // 2)))
+        if doc is not None:
+            starts = [j for j in range(1, n) if doc[0, seg[j]] != doc[0, seg[j - 1]]]
+            for j in starts[:4]:
+                slots |= set(range(max(0, j - R // 4), min(n, j + R // 4)))
         rows = seg[sorted(slots)]
         tail = seg[max(0, n - R):]
         out[g] = (rows, tail)
     return out
 
 
-def check_workload(config, variant, B, N, H, D, G, boundary, L, with_bwd):
+def check_workload(config, variant, B, N, H, D, G, boundary, L, with_bwd,
+                   doc=None):
     shift = G // 2
     sc = scale_for(D)
     heads = [1, H - 2]             # one head of each class
     say(f"config {config} B={B} N={N} H={H} D={D} G={G} L={L} "
-        f"boundary={boundary} bwd={with_bwd}")
+        f"boundary={boundary} bwd={with_bwd} "
+        f"documents={None if doc is None else int(doc.max()) + 1}")
     dev, host = gen(config, variant, B, N, H, D, L, heads, with_bwd)
+    dd = None if doc is None else torch.from_numpy(doc).cuda()
     o, lse = s2a.fwd(dev["q"], dev["k"], dev["v"], G=G, shift=shift,
-                     boundary=boundary, valid_len=L, scale=sc)
+                     boundary=boundary, valid_len=L, scale=sc, doc_ids=dd)
     if with_bwd:
         dq, dk, dv = s2a.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"],
                              G=G, shift=shift, boundary=boundary,
-                             valid_len=L, scale=sc)
+                             valid_len=L, scale=sc, doc_ids=dd)
     torch.cuda.synchronize()
     # padded rows are exactly zero everywhere (cheap to check in full)
     if L < N:
@@ -92,15 +100,16 @@ def check_workload(config, variant, B, N, H, D, G, boundary, L, with_bwd):
     errs = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
     for hi, h in enumerate(heads):
         cls = int(h >= H // 2)
-        for g, (rows, tail) in sample_rows(N, G, shift, boundary, L, cls).items():
+        for g, (rows, tail) in sample_rows(N, G, shift, boundary, L, cls,
+                                           doc).items():
             args = (host["q"], host["k"], host["v"])
             if with_bwd:
                 rdq, rdk, rdv, ro, rlse = oracle.backward(
                     *args, host["do"], G, shift, boundary, L, sc, heads=[hi],
-                    rows=rows)
+                    rows=rows, doc=doc)
             else:
                 ro, rlse = oracle.forward(*args, G, shift, boundary, L, sc,
-                                          heads=[hi], rows=rows)
+                                          heads=[hi], rows=rows, doc=doc)
             ri = torch.as_tensor(rows, device="cuda")
             ti = torch.as_tensor(tail, device="cuda")
             errs["o"].append(np.abs(o[:, ri, h].double().cpu().numpy()
@@ -152,3 +161,12 @@ def test_headline_shape_cyclic_32k():
 def test_ragged_100k(boundary):
     check_workload(5, boundary, 1, 102400, 32, 128, 25600, boundary, 100000,
                    True)
+
+
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.CYCLIC])
+def test_headline_shape_documents_32k(boundary):
+    # packed samples of mean length 1000 (as bench.py --docs 1000), the
+    # headline shape, the document-masked kernels
+    doc = syn.make_doc_ids(8000, 1, 32768, 1000)
+    check_workload(3, 3, 1, 32768, 32, 128, 8192, boundary, 32768, True,
+                   doc=doc)
