@@ -170,3 +170,13 @@ def test_headline_shape_documents_32k(boundary):
     doc = syn.make_doc_ids(8000, 1, 32768, 1000)
     check_workload(3, 3, 1, 32768, 32, 128, 8192, boundary, 32768, True,
                    doc=doc)
+
+
+@pytest.mark.parametrize("with_docs", [False, True])
+def test_long_group(with_docs):
+    # one group of 81,920 tokens (1,280 tiles of 64): under a document mask
+    # the tiles past the 1,024 whose IDs the kernels track are all walked
+    N = 81920
+    doc = syn.make_doc_ids(8100, 1, N, 3000) if with_docs else None
+    check_workload(6, int(with_docs), 1, N, 2, 64, N, syn.WRAP, N - 20, True,
+                   doc=doc)
