@@ -162,6 +162,71 @@ s2a_status s2attn_group_map(int N, int G, int shift, int boundary,
                             void *stream);
 
 /*
+ * Sequence-parallel shards: the attention of one slice of the sequence,
+ * as one of several devices holding consecutive slices would run it.
+ * PaperTrace LongLoRA §1.1 (the paragraphs on sequence-parallel
+ * communication): when rank boundaries fall on the unshifted groups'
+ * boundaries, only the shifted heads' groups cross them, and each slice
+ * needs the s = G/2 preceding tokens' K and V from its neighbour (a halo);
+ * the backward sends the gradients of those keys back.  Exchanging the
+ * halo is the caller's (a point-to-point send/receive per layer); these
+ * calls compute everything else.
+ *
+ * The slice is rows [row0, row0 + T) of a sequence of padded length N
+ * (one batch row), with row0 and T multiples of G.  Within it, heads are
+ * grouped exactly as by s2attn_fwd over the whole sequence, so the slices
+ * together give the same results (bit for bit wherever no halo partial
+ * sum is involved).
+ *
+ * s2attn_shard_halo (host only, no device work) names the halo rows:
+ *   left halo  global rows [*left_first, *left_first + *left_rows): the
+ *              rows before the slice in the shifted heads' group order
+ *              (row0-s .. row0-1; for the first slice under WRAP the valid
+ *              rows of N-s .. N-1; none for the first slice otherwise);
+ *   wrap halo  global rows [0, *wrap_rows): only the last slice under
+ *              CYCLIC (whose last shifted group starts with rows 0..s-1).
+ * Layouts (B = 1):
+ *   q, dout, o, dq    [T, H, D]  the slice's rows
+ *   k, v              point at the slice's row 0, [T, H, D] from there;
+ *                     the left halo must sit in the *left_rows rows just
+ *                     before it (k - left_rows*H*D ..), the wrap halo in
+ *                     rows [-2s, -2s + wrap_rows) relative to it
+ *   dk, dv            f32, the same layout as k: rows [0, T) get this
+ *                     slice's gradients; the halo rows of the shifted heads
+ *                     get the partial gradients this slice's queries give
+ *                     the neighbours' keys, to be sent back and added to
+ *                     their rows; other halo rows are not written
+ *   doc_ids           NULL, or int32 in k's layout (the halo rows' IDs
+ *                     included)
+ *   lse, delta_ws     f32 [H, T]
+ * Rows of the slice and of the halos must hold finite values (padded rows
+ * included).  valid_len is that of the whole sequence; rows at or past it
+ * are masked and zeroed as in s2attn_fwd / s2attn_bwd.  The shifted heads'
+ * dk, dv rows [T-s, T) of every slice but the last (under WRAP the last
+ * one's too) and, under CYCLIC, rows [0, s) of the first are partial
+ * until the halo partials that other slices computed for them are added.
+ * Checks: those of s2attn_fwd with B = 1, plus 0 <= row0, T > 0, row0 and
+ * T multiples of G, row0 + T <= N.
+ */
+s2a_status s2attn_shard_halo(int N, int row0, int T, int G, int shift,
+                             int boundary, int valid_len, int *left_first,
+                             int *left_rows, int *wrap_rows);
+
+s2a_status s2attn_fwd_shard(const void *q, const void *k, const void *v,
+                            void *o, int o_dtype, float *lse, int N, int row0,
+                            int T, int H, int D, int G, int shift,
+                            int boundary, int valid_len, const int *doc_ids,
+                            float scale, void *stream);
+
+s2a_status s2attn_bwd_shard(const void *q, const void *k, const void *v,
+                            const void *o, int o_dtype, const float *lse,
+                            const void *dout, float *dq, float *dk, float *dv,
+                            float *delta_ws, int N, int row0, int T, int H,
+                            int D, int G, int shift, int boundary,
+                            int valid_len, const int *doc_ids, float scale,
+                            void *stream);
+
+/*
  * Rotary position embedding (RoPE) at global positions: the prologue that
  * turns projected q and k into the rotated q and k the attention calls
  * take.  For pair i of every head (i = 0 .. D/2-1) at token (b, n):

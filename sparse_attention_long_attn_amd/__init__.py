@@ -7,9 +7,10 @@ marshals torch tensors into its calls.
 from . import _lib, work  # noqa: F401
 from ._lib import S2A_WRAP, S2A_SPLIT, S2AttnError, load  # noqa: F401
 from .ops import (fwd, bwd, bwd_preprocess, bwd_dkdv, bwd_dq,  # noqa: F401
-                  group_map, rope, rope_bwd, s2_attention, S2AttnFunction)
+                  group_map, rope, rope_bwd, s2_attention, S2AttnFunction,
+                  shard_halo, fwd_shard, bwd_shard)
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv",
            "bwd_dq", "group_map", "rope", "rope_bwd", "s2_attention",
-           "S2AttnFunction",
+           "S2AttnFunction", "shard_halo", "fwd_shard", "bwd_shard",
            "S2A_WRAP", "S2A_SPLIT", "S2AttnError", "load", "work"]

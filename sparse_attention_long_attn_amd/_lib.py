@@ -19,7 +19,8 @@ S2A_ROPE_HALF, S2A_ROPE_INTERLEAVED = 0, 1
 
 EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
            "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_group_map",
-           "s2attn_rope", "s2attn_rope_bwd",
+           "s2attn_rope", "s2attn_rope_bwd", "s2attn_shard_halo",
+           "s2attn_fwd_shard", "s2attn_bwd_shard",
            "s2attn_strerror", "s2attn_last_error", "s2attn_version")
 
 _lib = None
@@ -57,6 +58,17 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd_dq.restype = I
     lib.s2attn_group_map.argtypes = [I, I, I, I, I, P, P, P, P]
     lib.s2attn_group_map.restype = I
+    # N, row0, T, G, shift, boundary, valid_len, 3 int* outputs
+    lib.s2attn_shard_halo.argtypes = [I, I, I, I, I, I, I, P, P, P]
+    lib.s2attn_shard_halo.restype = I
+    # q, k, v, o, o_dtype, lse, N, row0, T, H, D, G, shift, boundary,
+    # valid_len, doc_ids, scale, stream
+    lib.s2attn_fwd_shard.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I,
+                                     I, I, P, F, P]
+    lib.s2attn_fwd_shard.restype = I
+    lib.s2attn_bwd_shard.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
+                                     I, I, I, I, I, I, I, I, I, P, F, P]
+    lib.s2attn_bwd_shard.restype = I
     # x, y, B, N, H, D, pos_ids, base, pos_scale, pairing, stream
     for fn in (lib.s2attn_rope, lib.s2attn_rope_bwd):
         fn.argtypes = [P, P, I, I, I, I, P, F, F, I, P]

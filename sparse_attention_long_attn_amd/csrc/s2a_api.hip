@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "s2attn.h"
 #include "s2a_device.h"
 #include "s2a_kernels.h"
@@ -61,22 +63,69 @@ S2AGeom make_geom(int N, int G, int shift, int boundary, int L) {
   g.s = (g.M == 1) ? 0 : shift;  // a single group has nothing to shift across
   g.boundary = boundary;
   g.L = L;
+  g.hl = 0;
+  g.hw = 0;
   return g;
 }
 
-S2AParams make_params(int B, int N, int H, int G, int shift, int boundary,
-                      int L, float scale, int tile_rows, const int *doc) {
+// Halo of the shard [row0, row0 + T) (see s2a_geom.h): exactly the rows
+// outside it that its valid queries read.  The left halo holds global
+// rows [left0, left0 + hl), the wrap halo rows [0, hw).  Under WRAP the
+// first shard's left halo is the end of the sequence, N-s .. N-1, of which
+// only the rows below L are kept (padding never enters a softmax, and
+// dropping it keeps the valid halo rows next to row 0).  A shard without
+// valid queries (L <= row0) reads nothing; the wrap halo is read only by
+// valid queries among the last s rows.
+void shard_halo(int N, int row0, int T, int G, int shift, int boundary,
+                int L, int &left0, int &hl, int &hw) {
+  const int s = (N / G == 1) ? 0 : shift;
+  left0 = row0;
+  hl = 0;
+  hw = 0;
+  if (s == 0 || L <= row0) return;
+  if (row0 > 0) {
+    left0 = row0 - s;
+    hl = s;
+  } else if (boundary == S2A_WRAP) {
+    left0 = N - s;
+    hl = L - left0 < 0 ? 0 : (L - left0 > s ? s : L - left0);
+  }
+  if (boundary == S2A_CYCLIC && row0 + T == N && L > N - s) hw = s;
+}
+
+S2AGeom make_shard_geom(int N, int row0, int T, int G, int shift,
+                        int boundary, int L) {
+  S2AGeom g;
+  g.N = T;
+  g.G = G;
+  g.M = T / G;
+  g.s = (N / G == 1) ? 0 : shift;
+  g.boundary = S2A_BOUNDARY_SHARD;
+  g.L = L - row0 < T ? L - row0 : T;  // positions are counted from row0
+  int left0;
+  shard_halo(N, row0, T, G, shift, boundary, L, left0, g.hl, g.hw);
+  return g;
+}
+
+S2AParams make_params_g(const S2AGeom &g, int B, int H, float scale,
+                        int tile_rows, const int *doc) {
   S2AParams p;
   p.doc = doc;
-  p.g = make_geom(N, G, shift, boundary, L);
+  p.g = g;
   p.B = B;
   p.H = H;
   p.ngmax = s2a_max_groups(p.g);
-  p.tiles = (G + tile_rows - 1) / tile_rows;
+  p.tiles = (g.G + tile_rows - 1) / tile_rows;
   p.units = B * H * p.ngmax;
   p.scale = scale;
   p.scale_log2 = scale * S2A_LOG2E;
   return p;
+}
+
+S2AParams make_params(int B, int N, int H, int G, int shift, int boundary,
+                      int L, float scale, int tile_rows, const int *doc) {
+  return make_params_g(make_geom(N, G, shift, boundary, L), B, H, scale,
+                       tile_rows, doc);
 }
 
 s2a_status hip_status(hipError_t e, const char *what) {
@@ -216,6 +265,101 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
   return hip_status(s2a_launch_bwd_dq(q, k, v, dout, lse, delta_ws, dq, D, p,
                                       (hipStream_t)stream),
                     "dQ launch");
+}
+
+namespace {
+
+// Shape checks of a shard: those of the whole sequence (one batch row),
+// and a slice [row0, row0 + T) of whole groups inside it.
+s2a_status check_shard(int N, int row0, int T, int H, int D, int G,
+                       int shift, int boundary, int valid_len) {
+  s2a_status st = check_shape(1, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (row0 < 0 || T <= 0 || row0 % G || T % G)
+    return fail(S2A_EINVAL, "row0=%lld and T=%lld must be multiples of G, "
+                "T > 0", row0, T);
+  if ((long long)row0 + T > N)
+    return fail(S2A_EINVAL, "row0 + T = %lld exceeds N=%lld",
+                (long long)row0 + T, N);
+  return S2A_OK;
+}
+
+s2a_status check_ptrs(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (!p) return fail(S2A_EINVAL, "NULL tensor pointer");
+  for (const void *p : ps)
+    if (!aligned16(p))
+      return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  return S2A_OK;
+}
+
+s2a_status check_common(const int *doc_ids, int o_dtype, float scale) {
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
+  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
+    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  return S2A_OK;
+}
+
+}  // namespace
+
+s2a_status s2attn_shard_halo(int N, int row0, int T, int G, int shift,
+                             int boundary, int valid_len, int *left_first,
+                             int *left_rows, int *wrap_rows) {
+  g_err[0] = 0;
+  s2a_status st = check_shard(N, row0, T, 2, 16, G, shift, boundary,
+                              valid_len);
+  if (st != S2A_OK) return st;
+  if (!left_first || !left_rows || !wrap_rows)
+    return fail(S2A_EINVAL, "NULL output pointer");
+  shard_halo(N, row0, T, G, shift, boundary, valid_len, *left_first,
+             *left_rows, *wrap_rows);
+  return S2A_OK;
+}
+
+s2a_status s2attn_fwd_shard(const void *q, const void *k, const void *v,
+                            void *o, int o_dtype, float *lse, int N, int row0,
+                            int T, int H, int D, int G, int shift,
+                            int boundary, int valid_len, const int *doc_ids,
+                            float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shard(N, row0, T, H, D, G, shift, boundary,
+                              valid_len);
+  if (st == S2A_OK) st = check_ptrs({q, k, v, o, lse});
+  if (st == S2A_OK) st = check_common(doc_ids, o_dtype, scale);
+  if (st != S2A_OK) return st;
+  const S2AGeom g = make_shard_geom(N, row0, T, G, shift, boundary,
+                                    valid_len);
+  const S2AParams p = make_params_g(g, 1, H, scale, s2a_fwd_tile_rows(D),
+                                    doc_ids);
+  return hip_status(s2a_launch_fwd(q, k, v, o, o_dtype == S2A_F32, lse, D, p,
+                                   (hipStream_t)stream),
+                    "shard forward launch");
+}
+
+s2a_status s2attn_bwd_shard(const void *q, const void *k, const void *v,
+                            const void *o, int o_dtype, const float *lse,
+                            const void *dout, float *dq, float *dk, float *dv,
+                            float *delta_ws, int N, int row0, int T, int H,
+                            int D, int G, int shift, int boundary,
+                            int valid_len, const int *doc_ids, float scale,
+                            void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shard(N, row0, T, H, D, G, shift, boundary,
+                              valid_len);
+  if (st == S2A_OK)
+    st = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, delta_ws});
+  if (st == S2A_OK) st = check_common(doc_ids, o_dtype, scale);
+  if (st != S2A_OK) return st;
+  const S2AGeom g = make_shard_geom(N, row0, T, G, shift, boundary,
+                                    valid_len);
+  const S2AParams p = make_params_g(g, 1, H, scale, 1, doc_ids);
+  return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
+                                   dq, dk, dv, delta_ws, D, p,
+                                   (hipStream_t)stream),
+                    "shard backward launch");
 }
 
 namespace {

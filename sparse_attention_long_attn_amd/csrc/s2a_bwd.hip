@@ -212,7 +212,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
       if (qsl < glen && ch * 8 < D) {
         const int qp = run.pos(qsl);
-        if (qp < L) {
+        if (qp < L && qp >= 0) {  // (halo rows: keys only)
           const size_t off = boff + (size_t)qp * rs + ch * 8;
           qv = *(const u32x4 *)(q + off);
           gv = *(const u32x4 *)(dout + off);
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       }
       if (qsl < glen) {
         const int qp = run.pos(qsl);
-        if (qp < L) {
+        if (qp < L && qp >= 0) {  // (halo rows: keys only)
           l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
@@ -415,6 +415,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
   const int glen = ut.glen;
   const int q0 = ut.tile * DQ_BQ;
   if (q0 >= glen) return;
+  if (run.pos(min(q0 + DQ_BQ, glen) - 1) < 0) return;  // halo rows only
   const int N = p.g.N, L = p.g.L;
   const size_t rs = (size_t)p.H * D;
   const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
@@ -423,8 +424,10 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_kernel(
 
   // This lane's query (one column of S^T, dP^T, dS^T).
   const int qslot = q0 + 32 * w + l32;
-  const bool qin = qslot < glen;
-  const int qpos = qin ? run.pos(qslot) : 0;
+  // (a shard's halo rows sit at negative positions and are keys only)
+  const int qp0 = qslot < glen ? run.pos(qslot) : -1;
+  const bool qin = qp0 >= 0;
+  const int qpos = qin ? qp0 : 0;
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
@@ -636,6 +639,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   const int glen = ut.glen;
   const int q0 = ut.tile * DQ_BQ;
   if (q0 >= glen) return;
+  if (run.pos(min(q0 + DQ_BQ, glen) - 1) < 0) return;  // halo rows only
   const int N = p.g.N, L = p.g.L;
   const size_t rs = (size_t)p.H * D;
   const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
@@ -644,8 +648,10 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
   const float c2 = p.scale_log2;
 
   const int qslot = q0 + 32 * w + l32;
-  const bool qin = qslot < glen;
-  const int qpos = qin ? run.pos(qslot) : 0;
+  // (a shard's halo rows sit at negative positions and are keys only)
+  const int qp0 = qslot < glen ? run.pos(qslot) : -1;
+  const bool qin = qp0 >= 0;
+  const int qpos = qin ? qp0 : 0;
   const bool qvalid = qin && qpos < L;
   const float l2 = qvalid ? lse[lrow + qpos] * S2A_LOG2E : INFINITY;
   const float dl = qvalid ? delta[lrow + qpos] : 0.f;
@@ -960,7 +966,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       if (DOC) qdst = p.doc[(size_t)ut.b * N + (qsl < glen ? run.pos(qsl) : 0)];
       if (qsl < glen) {
         const int qp = run.pos(qsl);
-        if (qp < L) {
+        if (qp < L && qp >= 0) {  // (halo rows: keys only)
           l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
@@ -977,13 +983,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   };
   auto issue_tile = [&](int q0, auto b) {
     char *qd = qbuf(b), *gd = gbuf(b);
-    if (tile_plain(run, glen, q0, BQ, L)) {
+    if (tile_plain(run, glen, q0, BQ, L, 0)) {
       const size_t r0 = (size_t)run.pos(q0) * rs;
       ld.fast_s(qbh + r0, qd);
       ld.fast_s(gbh + r0, gd);
     } else {
-      ld.general(qbh, rs, run, glen, q0, L, qd);
-      ld.general(gbh, rs, run, glen, q0, L, gd);
+      ld.general(qbh, rs, run, glen, q0, L, qd, 0);
+      ld.general(gbh, rs, run, glen, q0, L, gd, 0);
     }
   };
   // (rows trow and trow + 8 of a 16-row step have different swizzles)
@@ -1040,16 +1046,22 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       }
     return m;
   };
-  // body(masked, b, it): iteration it, whose tile sits in buffer b (= it % 2)
-  // body(masked, b, it): query tile it, held in buffer b (= it % 2).  Under
-  // a document mask a tile the workgroup does not walk is neither loaded
-  // nor computed: its iteration costs a barrier.
+  // Walk step it visits query tile it (it < 2, the tiles that can precede
+  // some of the keys) or it + skip: in a shard, the tiles before the first
+  // query of the slice hold halo rows only and are jumped over.
+  const int fq = s2a_first_query_slot(run, glen);
+  const int skip = max(0, (fq - k0) / BQ - 2);
+  // body(masked, b, it): walk step it, whose tile sits in buffer b
+  // (= it % 2).  Under a document mask a tile the workgroup does not walk
+  // is neither loaded nor computed: its step costs a barrier.
   auto body = [&](auto masked_tag, auto b, int it) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int buf = decltype(b)::value;
     using BN = std::integral_constant<int, 1 - buf>;
-    const int q0 = k0 + it * BQ;
-    const int pre = it + 1;  // tile loaded during this iteration
+    const int tt = MASKED ? it : it + skip;  // query tile of this step
+    const int q0 = k0 + tt * BQ;
+    // tile loaded during this step (the next step's)
+    const int pre = MASKED ? (it == 0 ? 1 : 2 + skip) : tt + 1;
     const bool pre_live = pre < nq && (!DOC || tile_bit(qlive, pre));
     if (pre_live) {
       fetch_stats(k0 + pre * BQ);
@@ -1072,7 +1084,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // block; keys outside the group need no mask (their garbage stays in
     // their own dK/dV column, written as zero at the end).
     constexpr int PIPE = 3;
-    bool live = !DOC || tile_bit(qlive, it), single = false;
+    bool live = !DOC || tile_bit(qlive, tt), single = false;
     if (DOC && live) {
       static_assert(BQ == 64, "one query document ID per lane");
       int qmn = qdocs[buf * BQ + lane], qmx = qmn;
@@ -1204,8 +1216,8 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     }  // live
-    // the next iteration reads tile it + 1 and its stats, both issued at
-    // the top of this one
+    // the next step reads tile pre and its stats, both issued at the top
+    // of this one
     wait_vm_all();
     if (pre_live) stage_stats(1 - buf);
     __syncthreads();
@@ -1215,9 +1227,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   static_assert((KV_BK + BQ - 1) / BQ == 2, "two masked iterations");
   body(std::true_type{}, B0{}, 0);
   if (nq > 1) body(std::true_type{}, B1{}, 1);
-  for (int it = 2; it < nq; it += 2) {
+  for (int it = 2; it + skip < nq; it += 2) {
     body(std::false_type{}, B0{}, it);
-    if (it + 1 < nq) body(std::false_type{}, B1{}, it + 1);
+    if (it + 1 + skip < nq) body(std::false_type{}, B1{}, it + 1);
   }
 
   mfma_agpr_drain();
@@ -1349,7 +1361,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
       if (s < glen && ch * 8 < D) {
         const int qp = run.pos(s);
-        if (qp < L) {
+        if (qp < L && qp >= 0) {  // (halo rows: keys only)
           const size_t off = boff + (size_t)qp * rs + ch * 8;
           qv = *(const u32x4 *)(q + off);
           gv = *(const u32x4 *)(dout + off);
@@ -1366,7 +1378,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
       if (s < glen) {
         const int qp = run.pos(s);
         if (DOC) dd = dbase[qp];
-        if (qp < L) {
+        if (qp < L && qp >= 0) {  // (halo rows: keys only)
           l2 = -lse[lrow + qp] / p.scale;
           dl = -delta[lrow + qp];
         }

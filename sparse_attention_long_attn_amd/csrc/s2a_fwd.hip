@@ -76,14 +76,17 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   if (!s2a_group(p.g, cls, gi, run, glen)) return;
   const int q0 = tile * FWD_BQ;
   if (q0 >= glen) return;
+  if (run.pos(min(q0 + FWD_BQ, glen) - 1) < 0) return;  // halo rows only
   const int N = p.g.N, L = p.g.L;
   const size_t rs = (size_t)p.H * D;  // elements between consecutive positions
   const size_t boff = (size_t)b * N * rs + (size_t)h * D;
 
   // This lane's query (one column of S^T).
   const int qslot = q0 + 32 * w + l32;
-  const bool qin = qslot < glen;
-  const int qpos = qin ? run.pos(qslot) : 0;
+  // (a shard's halo rows sit at negative positions and are keys only)
+  const int qp0 = qslot < glen ? run.pos(qslot) : -1;
+  const bool qin = qp0 >= 0;
+  const int qpos = qin ? qp0 : 0;
   const bool qvalid = qin && qpos < L;
   const int qdoc = DOC ? p.doc[(size_t)b * N + qpos] : 0;
 
@@ -333,14 +336,17 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   if (!s2a_group(p.g, cls, gi, run, glen)) return;
   const int q0 = tile * FWD_BQ;
   if (q0 >= glen) return;
+  if (run.pos(min(q0 + FWD_BQ, glen) - 1) < 0) return;  // halo rows only
   const int N = p.g.N, L = p.g.L;
   const size_t rs = (size_t)p.H * D;
   const size_t boff = (size_t)b * N * rs + (size_t)h * D;
   const bf16_t *kbh = k + boff, *vbh = v + boff;
 
   const int qslot = q0 + 32 * w + l32;
-  const bool qin = qslot < glen;
-  const int qpos = qin ? run.pos(qslot) : 0;
+  // (a shard's halo rows sit at negative positions and are keys only)
+  const int qp0 = qslot < glen ? run.pos(qslot) : -1;
+  const bool qin = qp0 >= 0;
+  const int qpos = qin ? qp0 : 0;
   const bool qvalid = qin && qpos < L;
   const int qdoc = DOC ? p.doc[(size_t)b * N + qpos] : 0;
   // Document IDs the wave's valid queries span: a key tile whose IDs all

@@ -19,6 +19,24 @@
 // positions form at most two increasing runs: slot j holds
 // base + j - (j >= cut ? jump : 0).  The kernels never build a rolled copy
 // of Q/K/V: a row's address is computed from its slot with pos().
+//
+// A shard (sequence parallelism, PaperTrace LongLoRA §1.1, the paragraphs
+// on distributed boundaries) is the slice [row0, row0 + T) of the rows,
+// with row0 and T multiples of G, so that only the shifted class has
+// groups that cross its edges.  Its geometry (S2A_BOUNDARY_SHARD) numbers
+// positions from row0: the slice holds 0 .. T-1, and the rows it reads
+// from other slices sit at negative positions, in front of row 0 of the
+// same buffers:
+//   left halo  -hl .. -1    the hl rows that precede the slice in the
+//                            shifted class's group order (rows row0-s ..
+//                            row0-1, or the valid part of N-s .. N-1 for
+//                            the first slice under WRAP);
+//   wrap halo  -2s .. -s-1  rows 0 .. s-1 (the last slice under CYCLIC,
+//                            whose last group starts with them).
+// Its groups: class 0 [kG, (k+1)G); class 1 first {left halo, 0 .. s-1},
+// then [kG - s, (k+1)G - s), and last {wrap halo if any, T-s .. T-1}.
+// Halo rows are keys only: a query counts when its position is >= 0,
+// which every position of the unsharded geometries is.
 #pragma once
 
 #ifndef __HIPCC__
@@ -29,14 +47,18 @@
 #define S2A_BOUNDARY_WRAP 0
 #define S2A_BOUNDARY_SPLIT 1
 #define S2A_BOUNDARY_CYCLIC 2
+#define S2A_BOUNDARY_SHARD 3  // internal: one slice of the rows (see above)
 
 struct S2AGeom {
-  int N;         // padded length
+  int N;         // padded length (a shard: its row count T)
   int G;         // group length
   int s;         // effective shift (0 if shift == 0 or N == G)
   int M;         // N / G
-  int boundary;  // S2A_BOUNDARY_WRAP, _SPLIT or _CYCLIC
-  int L;         // valid length
+  int boundary;  // S2A_BOUNDARY_WRAP, _SPLIT, _CYCLIC or _SHARD
+  int L;         // valid length (a shard: positions below L are valid;
+                 // it may be <= 0 or, for halo rows, cover negatives)
+  int hl;        // shard: rows of the left halo (0 .. s)
+  int hw;        // shard: rows of the wrap halo (0 or s)
 };
 
 // Slot -> original position of one group (see the file comment).
@@ -51,8 +73,10 @@ struct S2ARun {
 
 // Number of groups of head class cls.
 __host__ __device__ inline int s2a_num_groups(const S2AGeom &g, int cls) {
-  return (cls == 1 && g.s > 0 && g.boundary == S2A_BOUNDARY_SPLIT) ? g.M + 1
-                                                                     : g.M;
+  return (cls == 1 && g.s > 0 && (g.boundary == S2A_BOUNDARY_SPLIT ||
+                                  g.boundary == S2A_BOUNDARY_SHARD))
+             ? g.M + 1
+             : g.M;
 }
 
 // Groups of a class laid end to end; the largest count over both classes.
@@ -68,6 +92,20 @@ __host__ __device__ inline bool s2a_group(const S2AGeom &g, int cls, int gi,
   if (cls == 0 || g.s == 0) {
     run = {gi * g.G, g.G, 0};
     len = g.G;
+  } else if (g.boundary == S2A_BOUNDARY_SHARD) {
+    if (gi == 0) {  // left halo, then 0 .. s-1
+      len = g.hl + g.s;
+      run = {-g.hl, len, 0};
+    } else if (gi < g.M) {
+      run = {gi * g.G - g.s, g.G, 0};
+      len = g.G;
+    } else if (g.hw > 0) {  // wrap halo (-2s .. -s-1), then T-s .. T-1
+      len = g.hw + g.s;
+      run = {-2 * g.s, g.hw, -g.N - g.s + g.hw};
+    } else {  // T-s .. T-1 (the rest of the group is on the next slice)
+      run = {g.N - g.s, g.s, 0};
+      len = g.s;
+    }
   } else if (g.boundary == S2A_BOUNDARY_SPLIT) {
     const int base = gi == 0 ? 0 : g.s + (gi - 1) * g.G;
     len = (gi == 0 || gi == g.M) ? g.s : g.G;
@@ -83,6 +121,15 @@ __host__ __device__ inline bool s2a_group(const S2AGeom &g, int cls, int gi,
     len = g.G;
   }
   return true;
+}
+
+// First slot of a group whose position is >= 0 (holds a query of the
+// slice); 0 outside shards.  Used to skip query tiles of halo rows.
+__host__ __device__ inline int s2a_first_query_slot(const S2ARun &run,
+                                                    int len) {
+  if (run.base >= 0) return 0;
+  if (run.base + run.cut > 0) return -run.base;  // inside the first run
+  return run.cut < len ? run.cut : len;
 }
 
 // True if a slot of [j0, j1) (j0 < j1) holds a position >= L.  The largest

@@ -126,10 +126,12 @@ struct TileLoader {
   }
 
   // General rows: slot s0 + row of the group (run, glen); rows outside
-  // the group or at positions >= L read position 0 of the same (b, h)
-  // instead (finite data that the kernels mask out).
+  // the group, at positions >= L or below lo read position 0 of the same
+  // (b, h) instead (finite data that the kernels mask out).  Query tiles
+  // pass lo = 0: a shard's halo rows are keys only.
   __device__ void general(const bf16_t *gbh, size_t rs, const S2ARun &run,
-                          int glen, int s0, int L, char *lds) const {
+                          int glen, int s0, int L, char *lds,
+                          int lo = INT_MIN) const {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       // opaque copies keep the compiler from hoisting per-lane 64-bit
@@ -140,7 +142,7 @@ struct TileLoader {
       int pos = 0;
       if (s < glen) {
         pos = run.pos(s);
-        if (pos >= L) pos = 0;
+        if (pos >= L || pos < lo) pos = 0;
       }
       g2lds16(gbh + (size_t)pos * rs + co, lds + ldsb[i]);
     }
@@ -148,13 +150,15 @@ struct TileLoader {
 };
 
 // The tile [s0, s0 + rows) of a group is "plain" when every slot is inside
-// the group, inside one run, and at a position below L: then its rows are
-// contiguous in memory from slot s0's position.
+// the group, inside one run, and at a position in [lo, L): then its rows
+// are contiguous in memory from slot s0's position.
 __device__ __forceinline__ bool tile_plain(const S2ARun &run, int glen,
-                                           int s0, int rows, int L) {
+                                           int s0, int rows, int L,
+                                           int lo = INT_MIN) {
   if (s0 + rows > glen) return false;
   if (s0 < run.cut && s0 + rows > run.cut) return false;
-  return run.pos(s0) + rows <= L;
+  const int p0 = run.pos(s0);
+  return p0 + rows <= L && p0 >= lo;
 }
 
 __device__ __forceinline__ void wait_vm_all() {

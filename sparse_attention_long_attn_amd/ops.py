@@ -174,6 +174,122 @@ def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
                                  _docs(doc_ids, q), scale, _stream(q.device)))
 
 
+def shard_halo(N: int, row0: int, T: int, *, G: int, shift: int | None = None,
+               boundary="wrap", valid_len: int | None = None):
+    """Halo of the slice [row0, row0 + T) of a sequence of padded length N:
+    (left_first, left_rows, wrap_rows).  The left halo is global rows
+    [left_first, left_first + left_rows), stored right before the slice's
+    row 0; the wrap halo is rows [0, wrap_rows), stored 2s rows before it.
+    Host arithmetic of the library; nothing runs on the device."""
+    import ctypes
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    out = [ctypes.c_int(0) for _ in range(3)]
+    lib = _lib.load()
+    _lib.check(lib.s2attn_shard_halo(N, row0, T, G, shift,
+                                     _boundary(boundary), valid_len,
+                                     *(ctypes.byref(o) for o in out)))
+    return tuple(o.value for o in out)
+
+
+def _shard_args(q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len,
+                scale, doc_ext):
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, D] (one sequence)")
+    T, H, D = q.shape
+    for t in (q, k_ext, v_ext):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bfloat16 GPU tensors")
+    if k_ext.shape != v_ext.shape or k_ext.dim() != 3 \
+            or tuple(k_ext.shape[1:]) != (H, D) or k_ext.shape[0] < T:
+        raise ValueError("k, v must be [R + T, H, D]: R halo rows, then the "
+                         "slice's T rows")
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    R = k_ext.shape[0] - T
+    _, left_rows, wrap_rows = shard_halo(N, row0, T, G=G, shift=shift,
+                                         boundary=boundary,
+                                         valid_len=valid_len)
+    s = shift if N // G > 1 else 0
+    need = 2 * s if wrap_rows else left_rows
+    if R < need:
+        raise ValueError(f"k, v hold {R} halo rows; this slice needs {need}")
+    doc = None
+    if doc_ext is not None:
+        if doc_ext.dtype != torch.int32 or tuple(doc_ext.shape) != (R + T,) \
+                or not doc_ext.is_contiguous() or doc_ext.device != q.device:
+            raise ValueError("doc_ids must be a contiguous int32 [R + T] "
+                             "tensor in the layout of k")
+        doc = doc_ext.data_ptr() + 4 * R
+    off = R * H * D * 2  # bytes to the slice's row 0
+    return (T, H, D, shift, valid_len, scale, R, k_ext.data_ptr() + off,
+            v_ext.data_ptr() + off, doc)
+
+
+def fwd_shard(q, k_ext, v_ext, *, N: int, row0: int, G: int,
+              shift: int | None = None, boundary="wrap",
+              valid_len: int | None = None, scale: float | None = None,
+              out_dtype=torch.float32, doc_ext=None):
+    """Forward of the slice [row0, row0 + T) of a sequence of padded length
+    N (sequence parallelism).  q [T, H, D]; k_ext, v_ext [R + T, H, D]
+    with the slice's rows last and the halo (see shard_halo) in the R rows
+    before them; doc_ext: optional int32 [R + T] in the same layout.
+    Returns (o [T, H, D], lse [H, T] float32)."""
+    T, H, D, shift, valid_len, scale, R, kp, vp, doc = _shard_args(
+        q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len, scale,
+        doc_ext)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    o = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    odt = _lib.S2A_F32 if out_dtype == torch.float32 else _lib.S2A_BF16
+    lib = _lib.load()
+    _lib.check(lib.s2attn_fwd_shard(_ptr(q), kp, vp, _ptr(o), odt, _ptr(lse),
+                                    N, row0, T, H, D, G, shift,
+                                    _boundary(boundary), valid_len, doc,
+                                    scale, _stream(q.device)))
+    return o, lse
+
+
+def bwd_shard(q, k_ext, v_ext, o, lse, dout, *, N: int, row0: int, G: int,
+              shift: int | None = None, boundary="wrap",
+              valid_len: int | None = None, scale: float | None = None,
+              doc_ext=None):
+    """Backward of a slice from its forward's o and lse.  Returns (dq
+    [T, H, D], dk_ext, dv_ext [R + T, H, D]), float32: rows R.. are the
+    slice's keys, and the halo rows of the shifted heads hold the partial
+    gradients of the neighbours' keys (rows the kernels do not write stay
+    zero)."""
+    T, H, D, shift, valid_len, scale, R, kp, vp, doc = _shard_args(
+        q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len, scale,
+        doc_ext)
+    if dout.shape != q.shape or dout.dtype != torch.bfloat16 \
+            or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous bfloat16 [T, H, D] tensor")
+    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
+            or not o.is_contiguous():
+        raise ValueError("o must be a contiguous [T, H, D] float32/bfloat16 "
+                         "tensor")
+    if lse.dtype != torch.float32 or lse.shape != (H, T) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, T] tensor")
+    dq = torch.empty((T, H, D), dtype=torch.float32, device=q.device)
+    dk = torch.zeros((R + T, H, D), dtype=torch.float32, device=q.device)
+    dv = torch.zeros((R + T, H, D), dtype=torch.float32, device=q.device)
+    delta = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    off = R * H * D * 4
+    odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
+    lib = _lib.load()
+    _lib.check(lib.s2attn_bwd_shard(_ptr(q), kp, vp, _ptr(o), odt, _ptr(lse),
+                                    _ptr(dout), _ptr(dq), dk.data_ptr() + off,
+                                    dv.data_ptr() + off, _ptr(delta), N,
+                                    row0, T, H, D, G, shift,
+                                    _boundary(boundary), valid_len, doc,
+                                    scale, _stream(q.device)))
+    return dq, dk, dv
+
+
 PAIRINGS = {"half": _lib.S2A_ROPE_HALF, "interleaved": _lib.S2A_ROPE_INTERLEAVED,
             _lib.S2A_ROPE_HALF: _lib.S2A_ROPE_HALF,
             _lib.S2A_ROPE_INTERLEAVED: _lib.S2A_ROPE_INTERLEAVED}
