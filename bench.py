@@ -55,6 +55,10 @@ def parse():
                          "step under a document mask of packed samples with "
                          "geometric lengths of this mean (one JSON line; "
                          "useful work counts only same-document pairs)")
+    ap.add_argument("--shard", type=int, default=0, metavar="P",
+                    help="time one slice of the headline sequence cut into "
+                         "P slices (sequence parallelism, halo exchange "
+                         "not included)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a plain copy "
                          "kernel of known size, to calibrate HBM counters)")
@@ -300,6 +304,97 @@ def docs_bench(args):
     }), flush=True)
 
 
+def shard_bench(args):
+    """One slice of the headline sequence under sequence parallelism: the
+    headline workload cut into P slices on group edges, timed for a middle
+    slice (a left halo of s rows, no padding).  The halo exchange, a
+    point-to-point copy between devices, is not part of the timed work."""
+    import torch
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    from sparse_attention_long_attn_amd import work
+    cfg = WORKLOAD
+    N, H, D, G, L, bnd = (cfg[k] for k in ("N", "H", "D", "G", "L",
+                                           "boundary"))
+    P = args.shard
+    if N % P or (N // P) % G:
+        raise SystemExit(f"--shard {P}: slices of N/P rows must be whole "
+                         f"groups of {G}")
+    T, s = N // P, G // 2
+    r = 1 if P > 1 else 0
+    row0 = r * T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ins = syn.make_inputs(cfg["config"], 0, 1, N, H, D, with_do=True, L=L)
+    full = {t: torch.from_numpy(ins[t].view("int16")).view(torch.bfloat16)[0]
+            for t in ("q", "k", "v", "do")}
+    del ins
+    left0, hl, hw = s2a.shard_halo(N, row0, T, G=G, boundary=bnd,
+                                   valid_len=L)
+    R = 2 * s if hw else s
+
+    def ext(x):
+        e = torch.zeros((R + T, H, D), dtype=x.dtype)
+        e[R:] = x[row0:row0 + T]
+        if hl:
+            e[R - hl:R] = x[left0:left0 + hl]
+        if hw:
+            e[R - 2 * s:R - 2 * s + hw] = x[:hw]
+        return e.to(dev)
+
+    q = full["q"][row0:row0 + T].contiguous().to(dev)
+    do = full["do"][row0:row0 + T].contiguous().to(dev)
+    kx, vx = ext(full["k"]), ext(full["v"])
+    del full
+    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    dk, dv = (torch.zeros((R + T, H, D), dtype=torch.float32, device=dev)
+              for _ in range(2))
+    delta = torch.empty((H, T), dtype=torch.float32, device=dev)
+    kw = dict(N=N, row0=row0, G=G, boundary=bnd, valid_len=L)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def step(rec=False):
+        if rec:
+            ev[0].record()
+        s2a.fwd_shard(q, kx, vx, o=o, lse=lse, **kw)
+        if rec:
+            ev[1].record()
+        s2a.bwd_shard(q, kx, vx, o, lse, do, dq=dq, dk=dk, dv=dv, delta=delta,
+                      **kw)
+        if rec:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tf = tb = 0.0
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        tf += ev[0].elapsed_time(ev[1])
+        tb += ev[1].elapsed_time(ev[2])
+    tf, tb = tf / args.steps, tb / args.steps
+    c0, c1 = work.shard_pairs(N, row0, T, G, s, bnd, L)
+    pairs = (H // 2) * (c0 + c1)
+    useful = 14 * D * pairs
+    ms = tf + tb
+    print(json.dumps({
+        "metric": "S2-Attn fwd+bwd useful TFLOP/s of one sequence-parallel "
+                  "slice (halo exchange excluded)",
+        "value": round(useful / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "higher_is_better": True, "ms_per_step": round(ms, 4),
+        "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+        "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": f"slice {r} of {P} ({T} rows from {row0}) of "
+                               f"B=1 N={N} H={H} D={D} G={G} wrap",
+                   "halo_rows": hl, "allowed_pairs": pairs,
+                   "fraction_of_whole": round(
+                       pairs / work.total_pairs(1, N, H, G, s, bnd, L), 4)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -317,6 +412,9 @@ def main():
         return
     if args.docs:
         docs_bench(args)
+        return
+    if args.shard:
+        shard_bench(args)
         return
 
     import torch

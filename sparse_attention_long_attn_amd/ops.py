@@ -227,10 +227,21 @@ def _shard_args(q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len,
             v_ext.data_ptr() + off, doc)
 
 
+def _out(t, shape, dtype, dev, name, zero=False):
+    if t is None:
+        return (torch.zeros if zero else torch.empty)(shape, dtype=dtype,
+                                                      device=dev)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) \
+            or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous {dtype} {tuple(shape)} "
+                         f"tensor on {dev}")
+    return t
+
+
 def fwd_shard(q, k_ext, v_ext, *, N: int, row0: int, G: int,
               shift: int | None = None, boundary="wrap",
               valid_len: int | None = None, scale: float | None = None,
-              out_dtype=torch.float32, doc_ext=None):
+              out_dtype=torch.float32, doc_ext=None, o=None, lse=None):
     """Forward of the slice [row0, row0 + T) of a sequence of padded length
     N (sequence parallelism).  q [T, H, D]; k_ext, v_ext [R + T, H, D]
     with the slice's rows last and the halo (see shard_halo) in the R rows
@@ -241,8 +252,8 @@ def fwd_shard(q, k_ext, v_ext, *, N: int, row0: int, G: int,
         doc_ext)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be float32 or bfloat16")
-    o = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
-    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    o = _out(o, (T, H, D), out_dtype, q.device, "o")
+    lse = _out(lse, (H, T), torch.float32, q.device, "lse")
     odt = _lib.S2A_F32 if out_dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()
     _lib.check(lib.s2attn_fwd_shard(_ptr(q), kp, vp, _ptr(o), odt, _ptr(lse),
@@ -255,12 +266,12 @@ def fwd_shard(q, k_ext, v_ext, *, N: int, row0: int, G: int,
 def bwd_shard(q, k_ext, v_ext, o, lse, dout, *, N: int, row0: int, G: int,
               shift: int | None = None, boundary="wrap",
               valid_len: int | None = None, scale: float | None = None,
-              doc_ext=None):
+              doc_ext=None, dq=None, dk=None, dv=None, delta=None):
     """Backward of a slice from its forward's o and lse.  Returns (dq
     [T, H, D], dk_ext, dv_ext [R + T, H, D]), float32: rows R.. are the
     slice's keys, and the halo rows of the shifted heads hold the partial
-    gradients of the neighbours' keys (rows the kernels do not write stay
-    zero)."""
+    gradients of the neighbours' keys.  Rows the kernels do not write keep
+    what dk, dv held (zeros when they are allocated here)."""
     T, H, D, shift, valid_len, scale, R, kp, vp, doc = _shard_args(
         q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len, scale,
         doc_ext)
@@ -274,10 +285,11 @@ def bwd_shard(q, k_ext, v_ext, o, lse, dout, *, N: int, row0: int, G: int,
     if lse.dtype != torch.float32 or lse.shape != (H, T) \
             or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [H, T] tensor")
-    dq = torch.empty((T, H, D), dtype=torch.float32, device=q.device)
-    dk = torch.zeros((R + T, H, D), dtype=torch.float32, device=q.device)
-    dv = torch.zeros((R + T, H, D), dtype=torch.float32, device=q.device)
-    delta = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    f32, dev = torch.float32, q.device
+    dq = _out(dq, (T, H, D), f32, dev, "dq")
+    dk = _out(dk, (R + T, H, D), f32, dev, "dk", zero=True)
+    dv = _out(dv, (R + T, H, D), f32, dev, "dv", zero=True)
+    delta = _out(delta, (H, T), f32, dev, "delta")
     off = R * H * D * 4
     odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()

@@ -49,6 +49,27 @@ def allowed_pairs(N, G, shift, boundary, L):
     return tuple(out)
 
 
+def shard_pairs(N, row0, T, G, shift, boundary, L):
+    """Allowed pairs per head of class 0 and class 1 whose query lies in
+    the slice [row0, row0 + T): the work of that slice under sequence
+    parallelism (its keys may lie outside it).  A valid query at slot j of
+    a group reads the valid slots up to j."""
+    out = []
+    hi_q = min(L, row0 + T)
+    for cls in (0, 1):
+        tot = 0
+        for runs in _groups(N, G, shift, boundary, cls):
+            cnt = 0  # valid slots before the current run
+            for a, b in runs:
+                lo, hi = max(a, row0), min(b, hi_q)
+                if hi > lo:  # queries x in [lo, hi) read cnt + x - a + 1 keys
+                    n = hi - lo
+                    tot += n * (cnt - a + 1) + (lo + hi - 1) * n // 2
+                cnt += max(0, min(b, L) - a)
+        out.append(tot)
+    return tuple(out)
+
+
 def total_pairs(B, N, H, G, shift, boundary, L):
     c0, c1 = allowed_pairs(N, G, shift, boundary, L)
     return B * (H // 2) * (c0 + c1)

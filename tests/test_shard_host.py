@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from sparse_attention_long_attn_amd import _lib
+from sparse_attention_long_attn_amd import _lib, work
 
 BOUNDS = (oracle.WRAP, oracle.SPLIT, oracle.CYCLIC)
 
@@ -146,3 +146,25 @@ def test_shard_halo_rejects_bad_arguments():
         == _lib.S2A_EINVAL
     assert lib.s2attn_shard_halo(64, 0, 32, 16, 8, 0, 64, *refs) \
         == _lib.S2A_OK
+
+
+@pytest.mark.parametrize("boundary", BOUNDS)
+@pytest.mark.parametrize("N,G,P,L", [(64, 16, 4, 64), (64, 16, 4, 50),
+                                     (96, 16, 3, 90), (48, 8, 6, 7),
+                                     (64, 32, 2, 40), (32, 32, 1, 30)])
+def test_shard_pairs_match_oracle_enumeration(boundary, N, G, P, L):
+    # the work of one slice: allowed pairs whose query lies in it, counted
+    # from the oracle's adjacency rows of the slice
+    T = N // P
+    for half in (0, 1):
+        shift = half * G // 2
+        tot = [0, 0]
+        for r in range(P):
+            rows = np.arange(r * T, (r + 1) * T)
+            want = tuple(int(oracle.adjacency_block(c, rows, N, G, shift,
+                                                    boundary, L).sum())
+                         for c in (0, 1))
+            got = work.shard_pairs(N, r * T, T, G, shift, boundary, L)
+            assert got == want, (r, got, want)
+            tot = [tot[0] + got[0], tot[1] + got[1]]
+        assert tuple(tot) == work.allowed_pairs(N, G, shift, boundary, L)
