@@ -25,8 +25,20 @@ template <int D>
 struct SwTile {
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
   static constexpr int ROWB = D * 2;        // bytes per row
+  // Logical chunk c of row r sits at physical chunk c ^ swz(r).  The LDS
+  // has 64 banks of 4 bytes (256 bytes per sweep); a 16-byte read is served
+  // 16 lanes at a time and an 8-byte (transposing) read 32 lanes at a time.
+  // The operand reads (lane l: row l % 32, one chunk) need the 16 rows of a
+  // pass in distinct bank groups; the transposing reads (32 lanes: rows
+  // 4k .. 4k+3, chunks 4j .. 4j+3) need those four rows in distinct aligned
+  // groups of four chunks.  D = 128 (one row per sweep): swz is the 4x4
+  // transpose of r's low four bits.  D = 64 (two rows per sweep): rows of
+  // one parity take distinct chunks, rows 4k and 4k+2 different halves.
+  // Period 16 in r.
   __device__ static constexpr int swz(int r) {
-    return (((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1);
+    if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1);
   }
   // byte offset of logical chunk c of row r
   __device__ static constexpr int off(int r, int c) {
