@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -65,12 +66,29 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed: two
+    sources that differ only in comments or layout compile to the same
+    kernels."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the kernel sources' code (see code_tokens); ``read(name)``
+    returns a file's text (default: the working tree)."""
     csrc = os.path.join(ROOT, "sparse_attention_long_attn_amd", "csrc")
+    if read is None:
+        def read(name):
+            return open(os.path.join(csrc, name)).read()
+        names = os.listdir(csrc)
+    else:
+        names = read(None)
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(names):
         if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(code_tokens(read(f)).encode())
     return h.hexdigest()[:16]
 
 

@@ -196,8 +196,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
     }
   }
 
-  // Query-tile staging through registers.  Rows outside the group or padded
-  // get q = dO = 0, lse = +inf (so P = 0) and delta = 0 (so dS = 0).
+  // Query-tile staging through registers.  Rows outside the group, padded
+  // or in a shard's halo (negative positions: keys only) get q = dO = 0,
+  // lse = +inf (so P = 0) and delta = 0 (so dS = 0).
   u32x4 qst[NCH], gst[NCH];
   float l2st = INFINITY, dlst = 0.f;
   // DOC: document IDs of query q0 + tid and of the slot HOT_SPAN before it
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
       if (qsl < glen && ch * 8 < D) {
         const int qp = run.pos(qsl);
-        if (qp < L && qp >= 0) {  // (halo rows: keys only)
+        if (qp < L && qp >= 0) {
           const size_t off = boff + (size_t)qp * rs + ch * 8;
           qv = *(const u32x4 *)(q + off);
           gv = *(const u32x4 *)(dout + off);
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_kernel(
       }
       if (qsl < glen) {
         const int qp = run.pos(qsl);
-        if (qp < L && qp >= 0) {  // (halo rows: keys only)
+        if (qp < L && qp >= 0) {
           l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
@@ -961,7 +962,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   ld.init(w, lane);
   ld.init_rs(rs);
   // Per-row statistics of a query tile, through registers: rows outside
-  // the group or padded get lse = +inf (so P = 0) and delta = 0.
+  // the group, padded or in a shard's halo (negative positions: keys only)
+  // get lse = +inf (so P = 0) and delta = 0; their tile rows are loaded
+  // from position 0 (finite data the statistics zero out).
   float l2st = INFINITY, dlst = 0.f;
   int qdst = 0;  // document ID of query q0 + tid (DOC)
   auto fetch_stats = [&](int q0) {
@@ -972,7 +975,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       if (DOC) qdst = p.doc[(size_t)ut.b * N + (qsl < glen ? run.pos(qsl) : 0)];
       if (qsl < glen) {
         const int qp = run.pos(qsl);
-        if (qp < L && qp >= 0) {  // (halo rows: keys only)
+        if (qp < L && qp >= 0) {
           l2st = lse[lrow + qp];  // scaled at staging: no wait here
           dlst = delta[lrow + qp];
         }
@@ -1367,7 +1370,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
       u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
       if (s < glen && ch * 8 < D) {
         const int qp = run.pos(s);
-        if (qp < L && qp >= 0) {  // (halo rows: keys only)
+        if (qp < L && qp >= 0) {
           const size_t off = boff + (size_t)qp * rs + ch * 8;
           qv = *(const u32x4 *)(q + off);
           gv = *(const u32x4 *)(dout + off);
@@ -1379,12 +1382,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
     if (tid < KV_BQ) {
       const int s = q0 + tid;
       // initial S and dP accumulators, as in s2a_bwd_dkdv_sw_kernel
+      // (rows outside the group, padded or in a shard's halo: P = dS = 0)
       float l2 = -INFINITY, dl = 0.f;
       int dd = 0;
       if (s < glen) {
         const int qp = run.pos(s);
         if (DOC) dd = dbase[qp];
-        if (qp < L && qp >= 0) {  // (halo rows: keys only)
+        if (qp < L && qp >= 0) {
           l2 = -lse[lrow + qp] / p.scale;
           dl = -delta[lrow + qp];
         }
