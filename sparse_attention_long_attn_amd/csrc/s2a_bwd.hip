@@ -124,8 +124,11 @@ __device__ __forceinline__ UnitTile decode(const S2AParams &p, bool reverse) {
   const int u = lu * 8 + xcd;
   r.ok = u < p.units;
   if (!r.ok) return r;
-  const int gi = u % p.ngmax;
-  const int bh = u / p.ngmax;
+  // unit u = gi * (B*H) + (b*H + h): the units of one XCD (equal mod 8)
+  // are spread over the groups instead of sharing one group index, so the
+  // XCDs get equal work even when groups do not (under a document mask)
+  const int bh = u % (p.B * p.H);
+  const int gi = u / (p.B * p.H);
   r.h = bh % p.H;
   r.b = bh / p.H;
   r.cls = r.h >= (p.H >> 1);
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
     int mn = qdmn, mx = qdmx;
     wg_range<DQ_THREADS / 64>(mn, mx, rng, w, lane);
     doc_tiles<DQ_THREADS / 64>(p.doc + (size_t)ut.b * N, run, glen, L, 0,
-                               ntiles, mn, mx, 0, klive, nullptr, w, lane);
+                               ntiles, mn, mx, klive, nullptr, w, lane);
   }
   int it = DOC ? next_tile(klive, 0, ntiles) : 0;
   if (it < ntiles) issue(it * DQ_BK, 0);
@@ -745,10 +748,11 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
     // document, so the document mask must be applied)
     bool live = k0 <= wq_hi, docedge = false;
     if (DOC && live) {
-      int kmn = kdoc[buf][lane], kmx = kmn;
-      wave_minmax(kmn, kmx);
-      live = kmx >= qdmn && kmn <= qdmx;
-      docedge = !(kmn == kmx && qdmn == qdmx && kmn == qdmn);
+      // one key ID per lane; ballots rather than a cross-lane min/max,
+      // whose dependent shuffles would stall every tile
+      const int kd = kdoc[buf][lane];
+      live = __any(kd >= qdmn && kd <= qdmx);
+      docedge = !(qdmn == qdmx && __all(kd == qdmn));
     }
     if (live) {
       const char *Kb = Ks + buf * TILEB;
@@ -1028,7 +1032,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     int mn = kdmn, mx = kdmx;
     wg_range<THREADS / 64>(mn, mx, rng, w, lane);
     doc_tiles<THREADS / 64>(p.doc + (size_t)ut.b * N, run, glen, L, k0, nq,
-                            mn, mx, 0, qlive, nullptr, w, lane);
+                            mn, mx, qlive, nullptr, w, lane);
   }
   if (!DOC || tile_bit(qlive, 0)) {
     fetch_stats(k0);
@@ -1096,11 +1100,12 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     bool live = !DOC || tile_bit(qlive, tt), single = false;
     if (DOC && live) {
       static_assert(BQ == 64, "one query document ID per lane");
-      int qmn = qdocs[buf * BQ + lane], qmx = qmn;
-      wave_minmax(qmn, qmx);
-      live = qmx >= kdmn && qmn <= kdmx;
+      // (ballots rather than a cross-lane min/max, whose dependent
+      // shuffles would stall every tile)
+      const int qd = qdocs[buf * BQ + lane];
+      live = __any(qd >= kdmn && qd <= kdmx);
       // all of the tile's queries and the wave's keys in one document
-      single = qmn == qmx && kdmn == kdmx && qmn == kdmn;
+      single = kdmn == kdmx && __all(qd == kdmn);
     }
     if (live) {
     const unsigned dmask = DOC ? (single ? ~0u : same_doc_mask(buf)) : 0u;
@@ -1315,6 +1320,23 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
   const bool kvalid = kin && kpos < L;
   const int kdoc = DOC ? dbase[kpos] : 0;
 
+  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
+  // Under a document mask: the query tiles that can meet the workgroup's
+  // keys' documents and hold hot queries.  Most key tiles have none (hot
+  // rows sit at document starts): those workgroups stop here, before
+  // loading anything else.
+  if (DOC) {
+    int mn = kvalid ? kdoc : INT_MAX, mx = kvalid ? kdoc : INT_MIN;
+    wg_range<THREADS / 64>(mn, mx, rng, w, lane);
+    static_assert(HOT_SPAN == 64, "doc_tiles tests hot rows one tile back");
+    doc_tiles<THREADS / 64>(dbase, run, glen, L, k0, nq, mn, mx, qlive, qhot,
+                            w, lane);
+    bool work = nq > DOC_MAXT;  // (tiles past DOC_MAXT are all walked)
+    for (int k = 0; k < (min(nq, DOC_MAXT) + 31) / 32; ++k)
+      work = work || (__builtin_amdgcn_readfirstlane((int)(qlive[k] & qhot[k])) != 0);
+    if (!work) return;  // uniform: every wave read the same words
+  }
+
   bf16x8 kreg[Dm::KSTEPS], vreg[Dm::KSTEPS];
   {
     const size_t off = boff + (size_t)kpos * rs;
@@ -1340,15 +1362,6 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_lo_kernel(
     }
 
   bool any_hot = false;
-  const int nq = (glen - k0 + KV_BQ - 1) / KV_BQ;
-  // Under a document mask: the query tiles that can meet the workgroup's
-  // keys' documents and hold hot queries.
-  if (DOC) {
-    int mn = kvalid ? kdoc : INT_MAX, mx = kvalid ? kdoc : INT_MIN;
-    wg_range<THREADS / 64>(mn, mx, rng, w, lane);
-    doc_tiles<THREADS / 64>(dbase, run, glen, L, k0, nq, mn, mx, HOT_SPAN,
-                            qlive, qhot, w, lane);
-  }
   for (int it = 0; it < nq; ++it) {
     const int q0 = k0 + it * KV_BQ;
     if (!DOC && q0 >= HOT_SPAN) break;

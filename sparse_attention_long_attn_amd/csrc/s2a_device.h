@@ -25,7 +25,7 @@ struct S2AParams {
   int B, H;
   int ngmax;      // groups per head, laid out for both classes
   int tiles;      // row tiles per group (query tiles fwd, key tiles bwd)
-  int units;      // B * H * ngmax
+  int units;      // B * H * ngmax; unit gi * (B*H) + (b*H + h)
   float scale;    // softmax scale
   float scale_log2;  // scale * log2(e)
   const int *doc; // document IDs [B, N] (nullptr: no document mask)

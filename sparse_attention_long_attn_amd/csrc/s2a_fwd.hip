@@ -67,8 +67,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
   const int tile = p.tiles - 1 - (jj - lu * p.tiles);
   const int u = lu * 8 + xcd;
   if (u >= p.units) return;
-  const int gi = u % p.ngmax;
-  const int bh = u / p.ngmax;
+  // unit u = gi * (B*H) + (b*H + h): the units of one XCD (equal mod 8)
+  // are spread over the groups instead of sharing one group index, so the
+  // XCDs get equal work even when groups do not (under a document mask)
+  const int bh = u % (p.B * p.H);
+  const int gi = u / (p.B * p.H);
   const int h = bh % p.H, b = bh / p.H;
   const int cls = h >= (p.H >> 1);
   S2ARun run;
@@ -327,8 +330,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   const int tile = p.tiles - 1 - (jj - lu * p.tiles);
   const int u = lu * 8 + xcd;
   if (u >= p.units) return;
-  const int gi = u % p.ngmax;
-  const int bh = u / p.ngmax;
+  // unit u = gi * (B*H) + (b*H + h): the units of one XCD (equal mod 8)
+  // are spread over the groups instead of sharing one group index, so the
+  // XCDs get equal work even when groups do not (under a document mask)
+  const int bh = u % (p.B * p.H);
+  const int gi = u / (p.B * p.H);
   const int h = bh % p.H, b = bh / p.H;
   const int cls = h >= (p.H >> 1);
   S2ARun run;
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     int mn = qdmn, mx = qdmx;
     wg_range<FWD_THREADS / 64>(mn, mx, rng, w, lane);
     doc_tiles<FWD_THREADS / 64>(p.doc + (size_t)b * N, run, glen, L, 0,
-                                ntiles, mn, mx, 0, klive, nullptr, w, lane);
+                                ntiles, mn, mx, klive, nullptr, w, lane);
   }
   int it = DOC ? next_tile(klive, 0, ntiles) : 0;
   if (it < ntiles) issue(it * FWD_BK, 0);
@@ -439,10 +445,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     // document, so the document mask must be applied)
     bool live = k0 <= wq_hi, docedge = false;
     if (DOC && live) {
-      int kmn = kdoc[buf][lane], kmx = kmn;
-      wave_minmax(kmn, kmx);
-      live = kmx >= qdmn && kmn <= qdmx;
-      docedge = !(kmn == kmx && qdmn == qdmx && kmn == qdmn);
+      // one key ID per lane; ballots rather than a cross-lane min/max,
+      // whose dependent shuffles would stall every tile
+      const int kd = kdoc[buf][lane];
+      live = __any(kd >= qdmn && kd <= qdmx);
+      docedge = !(qdmn == qdmx && __all(kd == qdmn));
     }
     if (live) {
       const char *Kb = Ks + buf * TILEB;

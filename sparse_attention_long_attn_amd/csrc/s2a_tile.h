@@ -189,73 +189,56 @@ __device__ __forceinline__ void wait_vm() {
 // Document-mask tile lists.  A kernel that walks the 64-slot tiles
 // t0, t0 + 64, ... of a group needs only the tiles whose document IDs can
 // meet those of its own rows.  doc_tiles() marks, one bit per tile in the
-// LDS words live[], every tile j whose valid slots (inside the group, at a
-// position below L) hold IDs spanning a range that meets [lo, hi]; with
-// hot != nullptr it also marks tiles holding a "hot" slot s: s < span, or
-// an ID different from that of slot s - span (a row that sees few keys).
+// LDS words live[], every tile j with a valid slot (inside the group, at a
+// position below L) whose ID lies in [lo, hi] (the range of the caller's
+// own IDs, so a tile left unmarked shares no document with them); with
+// hot != nullptr it also marks tiles holding a "hot" valid slot s: s < 64,
+// or an ID different from that of slot s - 64 (a row that sees few keys).
 // Tiles past DOC_MAXT are all marked live (and hot): correct, not skipped.
 // Every thread of the workgroup calls it; it ends with a barrier.
 constexpr int DOC_MAXT = 1024;            // tiles tracked (groups <= 64K)
 constexpr int DOC_WORDS = DOC_MAXT / 32;
 
-// Bits 0, 2, 4, ... of x packed into bits 0..31.
-__device__ __forceinline__ unsigned even_bits(unsigned long long x) {
-  x &= 0x5555555555555555ull;
-  x = (x | (x >> 1)) & 0x3333333333333333ull;
-  x = (x | (x >> 2)) & 0x0f0f0f0f0f0f0f0full;
-  x = (x | (x >> 4)) & 0x00ff00ff00ff00ffull;
-  x = (x | (x >> 8)) & 0x0000ffff0000ffffull;
-  x = (x | (x >> 16)) & 0x00000000ffffffffull;
-  return (unsigned)x;
-}
-
 template <int NW>
 __device__ void doc_tiles(const int *docb, const S2ARun &run, int glen, int L,
-                          int t0, int ntiles, int lo, int hi, int span,
-                          unsigned *live, unsigned *hot, int w, int lane) {
+                          int t0, int ntiles, int lo, int hi, unsigned *live,
+                          unsigned *hot, int w, int lane) {
   const int nw = (min(ntiles, DOC_MAXT) + 31) / 32;
   for (int k = w; k < DOC_WORDS; k += NW) {
     unsigned lbits = ~0u, hbits = ~0u;  // beyond the tracked tiles: walk all
     if (k < nw) {
-      // Word k covers tiles 32k .. 32k+31; lane l reads the 32 slots of half
-      // l % 2 of tile 32k + l / 2 (all loads of a batch in flight at once).
-      const int sb = t0 + 64 * 32 * k + 32 * lane;
-      int mn = INT_MAX, mx = INT_MIN;
-      bool h = false;
+      // Word k covers tiles 32k .. 32k+31.  Load e of a lane reads slot
+      // lane of tile 32k + e, so each load instruction reads one tile's 64
+      // consecutive slots (coalesced) and a ballot per tile gives its bits.
+      // Padded slots are read at their own position too: the hot test
+      // compares with the slot one tile earlier whatever it holds.
+      const int sb = t0 + 64 * 32 * k + lane;
+      lbits = hbits = 0u;
+      int prev = 0;  // ID of slot sb - 64 (hot test of the word's first tile)
+      if (hot != nullptr && sb >= 64) prev = docb[run.pos(sb - 64)];
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
-        int d[16], r[16];
+        int d[16];
         bool vv[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int s = sb + 16 * part + e;
-          bool v = s < glen;
-          const int pos = v ? run.pos(s) : 0;
-          v = v && pos < L;
-          vv[e] = v;
+          const int s = sb + 64 * (16 * part + e);
+          const bool in = s < glen;
+          const int pos = in ? run.pos(s) : 0;
+          vv[e] = in && pos < L;
           d[e] = docb[pos];
-          r[e] = 0;
-          if (hot != nullptr) {
-            const int rs = s >= span ? s - span : 0;
-            r[e] = docb[run.pos(rs < glen ? rs : 0)];
-          }
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int s = sb + 16 * part + e;
-          if (vv[e]) {
-            mn = min(mn, d[e]);
-            mx = max(mx, d[e]);
-            if (hot != nullptr) h = h || s < span || r[e] != d[e];
+          const int j = 16 * part + e;
+          const int s = sb + 64 * j;
+          if (__any(vv[e] && d[e] >= lo && d[e] <= hi)) lbits |= 1u << j;
+          if (hot != nullptr) {
+            if (__any(vv[e] && (s < 64 || d[e] != prev))) hbits |= 1u << j;
+            prev = d[e];
           }
         }
       }
-      // the two halves of each tile
-      mn = min(mn, __shfl_xor(mn, 1, 64));
-      mx = max(mx, __shfl_xor(mx, 1, 64));
-      h = h || __shfl_xor((int)h, 1, 64);
-      lbits = even_bits(__ballot(mx >= lo && mn <= hi));
-      hbits = even_bits(__ballot(h));
     }
     if (lane == 0) {
       live[k] = lbits;
