@@ -1034,11 +1034,24 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     doc_tiles<THREADS / 64>(p.doc + (size_t)ut.b * N, run, glen, L, k0, nq,
                             mn, mx, qlive, nullptr, w, lane);
   }
-  if (!DOC || tile_bit(qlive, 0)) {
-    fetch_stats(k0);
+  // The walk: query tiles 0 and 1 (the ones that can precede some of the
+  // keys) run the masked body, later tiles the plain one.  In a shard the
+  // tiles before the first query of the slice hold halo rows only and are
+  // jumped over; under a document mask only the listed tiles are visited.
+  const int fq = s2a_first_query_slot(run, glen);
+  const int skip = max(0, (fq - k0) / BQ - 2);
+  auto next_walk = [&](int t) {
+    int n = t + 1;
+    if (n == 2) n += skip;
+    if (DOC) n = next_tile(qlive, n, nq);
+    return n;
+  };
+  const int first = DOC ? next_tile(qlive, 0, nq) : 0;
+  if (first < nq) {
+    fetch_stats(k0 + first * BQ);
     wait_vm_all();
     stage_stats(0);
-    issue_tile(k0, B0{});
+    issue_tile(k0 + first * BQ, B0{});
   }
   wait_vm_all();
   __syncthreads();
@@ -1059,23 +1072,16 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       }
     return m;
   };
-  // Walk step it visits query tile it (it < 2, the tiles that can precede
-  // some of the keys) or it + skip: in a shard, the tiles before the first
-  // query of the slice hold halo rows only and are jumped over.
-  const int fq = s2a_first_query_slot(run, glen);
-  const int skip = max(0, (fq - k0) / BQ - 2);
-  // body(masked, b, it): walk step it, whose tile sits in buffer b
-  // (= it % 2).  Under a document mask a tile the workgroup does not walk
-  // is neither loaded nor computed: its step costs a barrier.
-  auto body = [&](auto masked_tag, auto b, int it) {
+  // body(masked, b, tt): query tile tt, held in buffer b (walk steps
+  // alternate the buffers); returns the next tile of the walk, whose load
+  // it issues.
+  auto body = [&](auto masked_tag, auto b, int tt) -> int {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int buf = decltype(b)::value;
     using BN = std::integral_constant<int, 1 - buf>;
-    const int tt = MASKED ? it : it + skip;  // query tile of this step
     const int q0 = k0 + tt * BQ;
-    // tile loaded during this step (the next step's)
-    const int pre = MASKED ? (it == 0 ? 1 : 2 + skip) : tt + 1;
-    const bool pre_live = pre < nq && (!DOC || tile_bit(qlive, pre));
+    const int pre = next_walk(tt);  // tile loaded during this step
+    const bool pre_live = pre < nq;
     if (pre_live) {
       fetch_stats(k0 + pre * BQ);
       issue_tile(k0 + pre * BQ, BN{});
@@ -1097,7 +1103,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // block; keys outside the group need no mask (their garbage stays in
     // their own dK/dV column, written as zero at the end).
     constexpr int PIPE = 3;
-    bool live = !DOC || tile_bit(qlive, tt), single = false;
+    bool live = true, single = false;
     if (DOC && live) {
       static_assert(BQ == 64, "one query document ID per lane");
       // (ballots rather than a cross-lane min/max, whose dependent
@@ -1235,15 +1241,19 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     wait_vm_all();
     if (pre_live) stage_stats(1 - buf);
     __syncthreads();
+    return pre;
   };
 
-  // Iterations whose queries can precede some of the workgroup's keys.
-  static_assert((KV_BK + BQ - 1) / BQ == 2, "two masked iterations");
-  body(std::true_type{}, B0{}, 0);
-  if (nq > 1) body(std::true_type{}, B1{}, 1);
-  for (int it = 2; it + skip < nq; it += 2) {
-    body(std::false_type{}, B0{}, it);
-    if (it + 1 + skip < nq) body(std::false_type{}, B1{}, it + 1);
+  // The first two steps take the masked body: their tiles can hold queries
+  // that precede some of the keys (any later step's tile is past them).
+  static_assert((KV_BK + BQ - 1) / BQ == 2, "two masked steps");
+  int tt = first;
+  if (tt < nq) tt = body(std::true_type{}, B0{}, tt);
+  if (tt < nq) tt = body(std::true_type{}, B1{}, tt);
+  while (tt < nq) {
+    tt = body(std::false_type{}, B0{}, tt);
+    if (tt >= nq) break;
+    tt = body(std::false_type{}, B1{}, tt);
   }
 
   mfma_agpr_drain();
