@@ -60,6 +60,10 @@ def parse():
                     help="time one slice of the headline sequence cut into "
                          "P slices (sequence parallelism, halo exchange "
                          "not included)")
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="time the backward whose dQ kernel recomputes S "
+                         "and dP (s2attn_bwd) instead of the one that "
+                         "stores dS (s2attn_bwd_ds, the default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device (a plain copy "
                          "kernel of known size, to calibrate HBM counters)")
@@ -456,6 +460,10 @@ def main():
                   for _ in range(3))
     delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     kw = dict(G=G, shift=shift, boundary=bnd, valid_len=L)
+    # the backward stores dS (bf16, 2 bytes per allowed pair) in dK/dV and
+    # forms dQ from it, unless --recompute-dq asks for the other backward
+    stored = not args.recompute_dq
+    ws = s2a.ds_workspace(q, G=G, shift=shift, boundary=bnd) if stored else None
 
     def step(ev=None):
         if ev is not None:
@@ -466,10 +474,16 @@ def main():
         s2a.bwd_preprocess(o, do, delta)
         if ev is not None:
             ev[2].record()
-        s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
+        if stored:
+            s2a.bwd_dkdv_ds(q, k, v, lse, delta, do, dk, dv, ws, **kw)
+        else:
+            s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
         if ev is not None:
             ev[3].record()
-        s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+        if stored:
+            s2a.bwd_dq_ds(k, ws, dq, **kw)
+        else:
+            s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
         if ev is not None:
             ev[4].record()
 
@@ -510,12 +524,14 @@ def main():
 
     # useful work of each kernel: QK^T and PV (fwd); the backward's 10*D
     # per pair is dV, dK, dP and S in the dK/dV kernel (8*D) and dQ (2*D)
-    # in the dQ kernel, which also recomputes S and dP (not counted)
+    # in the dQ kernel (which, with --recompute-dq, also recomputes S and
+    # dP: not counted)
     D_pairs = f_fwd // (4 * D)
     kernels = {
         "s2a_fwd_sw_kernel": (fwd_ms, f_fwd),
         "s2a_bwd_dkdv_sw_kernel": (dkdv_ms, 8 * D * D_pairs),
-        "s2a_bwd_dq_sw_kernel": (dq_ms, 2 * D * D_pairs),
+        ("s2a_bwd_dq_ds_kernel" if stored else "s2a_bwd_dq_sw_kernel"):
+            (dq_ms, 2 * D * D_pairs),
     }
     dom = max(kernels, key=lambda n: kernels[n][0])
     dms, dfl = kernels[dom]
@@ -549,6 +565,8 @@ def main():
                    "head_dim": D, "group": G, "boundary": "wrap",
                    "valid_len": L, "parallelism": "none (1 GPU)"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "backward": "stored dS" if stored else "recomputed S, dP for dQ",
+        "ds_workspace_bytes": ws.numel() if stored else 0,
         "fwd_ms": round(fwd_ms, 4),
         "bwd_preprocess_ms": round(pre_ms, 4),
         "bwd_dkdv_ms": round(dkdv_ms, 4),

@@ -50,6 +50,8 @@
 #ifndef S2ATTN_H
 #define S2ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -142,6 +144,54 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
                          int D, int G, int shift, int boundary,
                          int valid_len, const int *doc_ids, float scale,
                          void *stream);
+
+/*
+ * The backward with dS stored instead of recomputed.  Same gradients as
+ * s2attn_bwd, to the same tolerance (not bitwise: dQ sums in another
+ * order); D in {64, 128} and no document mask.  The dK/dV stage keeps
+ * dz_xy (above) in bf16, as its dK product uses it, for every allowed pair
+ * in a caller-provided workspace, and the dQ stage forms
+ * dq[x] = scale * sum_y dz_xy k[y] from it, so S and dP are computed once
+ * (PaperTrace LongLoRA §3: the gradient of a logit is the only term dq
+ * needs).  The queries that see fewest keys (the first 128 slots of each
+ * group) also keep the bf16 rounding residual of their dz.
+ *
+ * ds_ws: device workspace of at least s2attn_bwd_ds_workspace() bytes,
+ * 16-byte aligned, owned by the caller; its contents are scratch (written
+ * by the dK/dV stage, read by the dQ stage; neither zeroes it first).
+ * About 2 bytes per allowed pair: 8.7 GB for B=1, N=32768, H=32, G=8192.
+ * Other arguments as for s2attn_bwd.  Errors: S2A_EUNSUPPORTED for other
+ * D, S2A_EINVAL for a missing, misaligned or short workspace, as well as
+ * every check of s2attn_bwd.
+ */
+s2a_status s2attn_bwd_ds_workspace(int B, int N, int H, int D, int G,
+                                   int shift, int boundary, size_t *bytes);
+
+s2a_status s2attn_bwd_ds(const void *q, const void *k, const void *v,
+                         const void *o, int o_dtype, const float *lse,
+                         const void *dout, float *dq, float *dk, float *dv,
+                         float *delta_ws, void *ds_ws, size_t ds_ws_bytes,
+                         int B, int N, int H, int D, int G, int shift,
+                         int boundary, int valid_len, float scale,
+                         void *stream);
+
+/*
+ * The stages of s2attn_bwd_ds after s2attn_bwd_preprocess, for callers
+ * that time them separately: s2attn_bwd_dkdv_ds writes dk, dv and fills
+ * ds_ws; s2attn_bwd_dq_ds then writes dq (every row) from ds_ws and k
+ * alone.  They must run in this order, with the same geometry.
+ */
+s2a_status s2attn_bwd_dkdv_ds(const void *q, const void *k, const void *v,
+                              const float *lse, const float *delta_ws,
+                              const void *dout, float *dk, float *dv,
+                              void *ds_ws, size_t ds_ws_bytes, int B, int N,
+                              int H, int D, int G, int shift, int boundary,
+                              int valid_len, float scale, void *stream);
+
+s2a_status s2attn_bwd_dq_ds(const void *k, const void *ds_ws,
+                            size_t ds_ws_bytes, float *dq, int B, int N, int H,
+                            int D, int G, int shift, int boundary,
+                            int valid_len, float scale, void *stream);
 
 /*
  * Group index maps, computed on the device by the same group geometry the

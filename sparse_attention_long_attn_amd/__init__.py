@@ -8,9 +8,12 @@ from . import _lib, work  # noqa: F401
 from ._lib import S2A_WRAP, S2A_SPLIT, S2AttnError, load  # noqa: F401
 from .ops import (fwd, bwd, bwd_preprocess, bwd_dkdv, bwd_dq,  # noqa: F401
                   group_map, rope, rope_bwd, s2_attention, S2AttnFunction,
-                  shard_halo, fwd_shard, bwd_shard)
+                  shard_halo, fwd_shard, bwd_shard, ds_workspace_bytes,
+                  ds_workspace, bwd_ds, bwd_dkdv_ds, bwd_dq_ds)
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv",
            "bwd_dq", "group_map", "rope", "rope_bwd", "s2_attention",
            "S2AttnFunction", "shard_halo", "fwd_shard", "bwd_shard",
+           "ds_workspace_bytes", "ds_workspace", "bwd_ds", "bwd_dkdv_ds",
+           "bwd_dq_ds",
            "S2A_WRAP", "S2A_SPLIT", "S2AttnError", "load", "work"]

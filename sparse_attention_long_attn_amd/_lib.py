@@ -21,6 +21,8 @@ EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
            "s2attn_bwd_dkdv", "s2attn_bwd_dq", "s2attn_group_map",
            "s2attn_rope", "s2attn_rope_bwd", "s2attn_shard_halo",
            "s2attn_fwd_shard", "s2attn_bwd_shard",
+           "s2attn_bwd_ds_workspace", "s2attn_bwd_ds", "s2attn_bwd_dkdv_ds",
+           "s2attn_bwd_dq_ds",
            "s2attn_strerror", "s2attn_last_error", "s2attn_version")
 
 _lib = None
@@ -69,6 +71,19 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd_shard.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, I, I, P, F, P]
     lib.s2attn_bwd_shard.restype = I
+    Z = ctypes.c_size_t
+    # B, N, H, D, G, shift, boundary, bytes*
+    lib.s2attn_bwd_ds_workspace.argtypes = [I, I, I, I, I, I, I,
+                                            ctypes.POINTER(Z)]
+    lib.s2attn_bwd_ds_workspace.restype = I
+    lib.s2attn_bwd_ds.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, Z,
+                                  I, I, I, I, I, I, I, I, F, P]
+    lib.s2attn_bwd_ds.restype = I
+    lib.s2attn_bwd_dkdv_ds.argtypes = [P, P, P, P, P, P, P, P, P, Z,
+                                       I, I, I, I, I, I, I, I, F, P]
+    lib.s2attn_bwd_dkdv_ds.restype = I
+    lib.s2attn_bwd_dq_ds.argtypes = [P, P, Z, P, I, I, I, I, I, I, I, I, F, P]
+    lib.s2attn_bwd_dq_ds.restype = I
     # x, y, B, N, H, D, pos_ids, base, pos_scale, pairing, stream
     for fn in (lib.s2attn_rope, lib.s2attn_rope_bwd):
         fn.argtypes = [P, P, I, I, I, I, P, F, F, I, P]

@@ -111,6 +111,7 @@ S2AParams make_params_g(const S2AGeom &g, int B, int H, float scale,
                         int tile_rows, const int *doc) {
   S2AParams p;
   p.doc = doc;
+  p.dsws = nullptr;
   p.g = g;
   p.B = B;
   p.H = H;
@@ -264,6 +265,121 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
                                   scale, 1, doc_ids);
   return hip_status(s2a_launch_bwd_dq(q, k, v, dout, lse, delta_ws, dq, D, p,
                                       (hipStream_t)stream),
+                    "dQ launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks of the stored-dS variant: D in {64, 128}, a workspace of at least
+// s2attn_bwd_ds_workspace bytes, 16-byte aligned.  Sets p.dsws.
+s2a_status check_ds(int D, void *ds_ws, size_t ds_ws_bytes, S2AParams &p) {
+  if (D != 64 && D != 128)
+    return fail(S2A_EUNSUPPORTED,
+                "the stored-dS backward needs D in {64,128}, not %lld", D);
+  const long double need = s2a_ds_workspace_bytes(p);
+  if (need > 4.0e18L)
+    return fail(S2A_EINVAL, "dS workspace too large for one launch");
+  if (!ds_ws) return fail(S2A_EINVAL, "NULL dS workspace");
+  if (!aligned16(ds_ws))
+    return fail(S2A_EINVAL, "dS workspace must be 16-byte aligned");
+  if ((long double)ds_ws_bytes < need)
+    return fail(S2A_EINVAL, "dS workspace of %lld bytes, %lld needed",
+                (long long)ds_ws_bytes, (long long)need);
+  p.dsws = ds_ws;
+  return S2A_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+s2a_status s2attn_bwd_ds_workspace(int B, int N, int H, int D, int G,
+                                   int shift, int boundary, size_t *bytes) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, N);
+  if (st != S2A_OK) return st;
+  if (!bytes) return fail(S2A_EINVAL, "NULL result pointer");
+  if (D != 64 && D != 128)
+    return fail(S2A_EUNSUPPORTED,
+                "the stored-dS backward needs D in {64,128}, not %lld", D);
+  const S2AParams p = make_params(B, N, H, G, shift, boundary, N, 1.f, 1,
+                                  nullptr);
+  const long double need = s2a_ds_workspace_bytes(p);
+  if (need > 4.0e18L)
+    return fail(S2A_EINVAL, "dS workspace too large for one launch");
+  *bytes = (size_t)need;
+  return S2A_OK;
+}
+
+s2a_status s2attn_bwd_ds(const void *q, const void *k, const void *v,
+                         const void *o, int o_dtype, const float *lse,
+                         const void *dout, float *dq, float *dk, float *dv,
+                         float *delta_ws, void *ds_ws, size_t ds_ws_bytes,
+                         int B, int N, int H, int D, int G, int shift,
+                         int boundary, int valid_len, float scale,
+                         void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws)
+    return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(delta_ws))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
+    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len, scale, 1,
+                            nullptr);
+  st = check_ds(D, ds_ws, ds_ws_bytes, p);
+  if (st != S2A_OK) return st;
+  return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
+                                   dq, dk, dv, delta_ws, D, p,
+                                   (hipStream_t)stream),
+                    "backward launch");
+}
+
+s2a_status s2attn_bwd_dkdv_ds(const void *q, const void *k, const void *v,
+                              const float *lse, const float *delta_ws,
+                              const void *dout, float *dk, float *dv,
+                              void *ds_ws, size_t ds_ws_bytes, int B, int N,
+                              int H, int D, int G, int shift, int boundary,
+                              int valid_len, float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_grad_stage(q, k, v, lse, delta_ws, dout, dk, dv, B, N,
+                                   H, D, G, shift, boundary, valid_len, scale);
+  if (st != S2A_OK) return st;
+  S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len, scale, 1,
+                            nullptr);
+  st = check_ds(D, ds_ws, ds_ws_bytes, p);
+  if (st != S2A_OK) return st;
+  return hip_status(s2a_launch_bwd_dkdv(q, k, v, dout, lse, delta_ws, dk, dv,
+                                        D, p, (hipStream_t)stream),
+                    "dK/dV launch");
+}
+
+s2a_status s2attn_bwd_dq_ds(const void *k, const void *ds_ws,
+                            size_t ds_ws_bytes, float *dq, int B, int N, int H,
+                            int D, int G, int shift, int boundary,
+                            int valid_len, float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!k || !dq) return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(k) || !aligned16(dq))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len, scale, 1,
+                            nullptr);
+  st = check_ds(D, const_cast<void *>(ds_ws), ds_ws_bytes, p);
+  if (st != S2A_OK) return st;
+  return hip_status(s2a_launch_bwd_dq(nullptr, k, nullptr, nullptr, nullptr,
+                                      nullptr, dq, D, p, (hipStream_t)stream),
                     "dQ launch");
 }
 

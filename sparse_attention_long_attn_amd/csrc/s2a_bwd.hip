@@ -51,6 +51,41 @@ constexpr int DQ_MINBLOCKS = 512 / DQ_THREADS;  // two waves per SIMD
 // that involve hot queries take P and dS as bf16 hi + lo parts.
 constexpr int HOT_SPAN = 64;
 
+// dS workspace.  The variant of the backward that stores dS in dK/dV, so
+// that dQ = scale dS K needs no recomputation of S and dP, keeps bf16 dS
+// in blocks of 64 queries x 128 keys (16 KiB): query tile qt (64 slots of
+// the group) against key block kb (the 128 keys of one dK/dV workgroup).
+// Unit u (a (b, h, group), numbered as the grids number them) owns
+// nkb (nkb + 1) + 2 blocks, nkb = ceil(G / 128): first the blocks with
+// qt >= 2 kb (the others hold only queries that precede every key),
+// kb-major, then two residual blocks, kb = 0 and qt = 0, 1, holding
+// dS - bf16(dS).  Queries in the first 128 slots of a group see at most
+// 128 keys, all of them in key block 0; their dS entries are the largest
+// (about 1 / (number of keys seen)) and their bf16 rounding is not averaged
+// away.  Later rows see more than 128 keys, so the rounding error of their
+// dQ is at least ten times smaller and needs no residual.
+// Inside a block, chunk (w, qb, h2) of 1 KiB holds, for each of the 32
+// keys of dK/dV wave w, the 16 bytes of dS against the queries
+// 32 qb + 16 h2 + {4a .. 4a+3, 8+4a .. 8+4a+3} (a = 0, 1: the lane half
+// that computed them).  Lane (a, key) sits at 16-byte slot
+// 32 a + (key ^ 4 (a + 2 h2)): the dQ kernel's transposing reads then
+// touch every LDS bank once.
+constexpr int DS_BLOCK = 16384;
+__host__ __device__ inline int ds_nkb(int G) { return (G + KV_BK - 1) / KV_BK; }
+__device__ inline size_t ds_unit(int u, int nkb) {
+  return (size_t)u * ((size_t)nkb * (nkb + 1) + 2);
+}
+__device__ inline size_t ds_block(int u, int nkb, int kb, int qt) {
+  // kb (2 nkb - kb + 1) = blocks of the key blocks before kb
+  return ds_unit(u, nkb) + (size_t)kb * (2 * nkb - kb + 1) + (qt - 2 * kb);
+}
+__device__ inline size_t ds_res_block(int u, int nkb, int tt) {
+  return ds_unit(u, nkb) + (size_t)nkb * (nkb + 1) + tt;
+}
+__device__ inline int ds_slot(int a, int key, int h2) {
+  return 32 * a + (key ^ (4 * (a + 2 * h2)));
+}
+
 template <int D>
 struct BwdDims {
   static constexpr int DP = D < 32 ? 32 : D;
@@ -110,7 +145,7 @@ __global__ __launch_bounds__(256) void s2a_bwd_pre_kernel(
 // one XCD and share its L2.
 struct UnitTile {
   S2ARun run;
-  int b, h, cls, glen, tile;
+  int b, h, cls, glen, tile, u;
   bool ok;
 };
 
@@ -122,6 +157,7 @@ __device__ __forceinline__ UnitTile decode(const S2AParams &p, bool reverse) {
   const int t = jj - lu * p.tiles;
   r.tile = reverse ? p.tiles - 1 - t : t;
   const int u = lu * 8 + xcd;
+  r.u = u;
   r.ok = u < p.units;
   if (!r.ok) return r;
   // unit u = gi * (B*H) + (b*H + h): the units of one XCD (equal mod 8)
@@ -885,7 +921,7 @@ __global__ __launch_bounds__(DQ_THREADS, DQ_MINBLOCKS) void s2a_bwd_dq_sw_kernel
 // a body's LDS reads do not touch the buffer its direct loads are filling;
 // with one array and a computed buffer it waited for those loads (the next
 // tile) before the first read, which serialised load and compute.
-template <int D, int BQ, bool DOC>
+template <int D, int BQ, bool DOC, bool DS>
 __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
@@ -1178,6 +1214,38 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       tq[qb][st] = cat4(lds_read_tr((const bf16_t *)(qr + troff[db])),
                         lds_read_tr((const bf16_t *)(qr + troff8[db])));
     };
+    // DS: block qb's dS (bf16, as the dK product takes it) to the tile's
+    // workspace block, zero for keys outside the group or padded; in key
+    // block 0, on its two masked tiles, also the rounding residual
+    // dS - bf16(dS).  Nontemporal: dQ reads it back from HBM much later.
+    auto store_ds = [&](int qb) {
+      if constexpr (DS) {
+        const int nkb = ds_nkb(p.g.G);
+        const size_t cb = (size_t)((w * 2 + qb) * 2) * 1024;
+        char *blk = (char *)p.dsws +
+                    ds_block(ut.u, nkb, ut.tile, 2 * ut.tile + tt) * DS_BLOCK + cb;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int off = h2 * 1024 + 16 * ds_slot(hf, l32, h2);
+          u32x4 val = {0u, 0u, 0u, 0u};
+          if (kvalid) val = __builtin_bit_cast(u32x4, sb[qb][h2]);
+          __builtin_nontemporal_store(val, (u32x4 *)(blk + off));
+          if (MASKED && ut.tile == 0) {
+            char *res = (char *)p.dsws + ds_res_block(ut.u, nkb, tt) * DS_BLOCK + cb;
+            const int e0 = 8 * h2;
+            const bf16x8 hi = sb[qb][h2];
+            const bf16x8 lo = to_bf16x8(
+                dP[qb][e0] - (float)hi[0], dP[qb][e0 + 1] - (float)hi[1],
+                dP[qb][e0 + 2] - (float)hi[2], dP[qb][e0 + 3] - (float)hi[3],
+                dP[qb][e0 + 4] - (float)hi[4], dP[qb][e0 + 5] - (float)hi[5],
+                dP[qb][e0 + 6] - (float)hi[6], dP[qb][e0 + 7] - (float)hi[7]);
+            u32x4 rv = {0u, 0u, 0u, 0u};
+            if (kvalid) rv = __builtin_bit_cast(u32x4, lo);
+            __builtin_nontemporal_store(rv, (u32x4 *)(res + off));
+          }
+        }
+      }
+    };
     auto spmfma = [&](int qb, int t) {
       S[qb] = mfma32(aq[qb][t], kreg[t], S[qb]);
       dP[qb] = mfma32(ag[qb][t], vreg[t], dP[qb]);
@@ -1210,7 +1278,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 #pragma unroll
       for (int e = 0; e < EPS; ++e) elem(0, EPS * t + e);
       if (EPS * (t + 1) == 8) pack(0, 0);
-      if (t == KSTEPS - 1) pack(0, 1);
+      if (t == KSTEPS - 1) {
+        pack(0, 1);
+        store_ds(0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // P3
@@ -1224,7 +1295,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 #pragma unroll
       for (int e = 0; e < EPS; ++e) elem(1, EPS * st + e);
       if (EPS * (st + 1) == 8) pack(1, 0);
-      if (st == NST - 1) pack(1, 1);
+      if (st == NST - 1) {
+        pack(1, 1);
+        store_ds(1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // P4
@@ -1274,6 +1348,174 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
         }
         *(f32x4 *)(dk + row + d) = kk;
         *(f32x4 *)(dv + row + d) = vv;
+      }
+  }
+}
+
+// dQ from the stored dS (D in {64, 128}): dQ^T += K^T dS^T over the key
+// blocks 0 .. j of query tile j (128 queries), and for tile 0 over the
+// residual blocks as well.  Nothing is recomputed, so the kernel
+// streams dS from HBM (2 bytes per allowed pair).  Stages of 64 keys flow
+// through a ring of DSQ_STAGES LDS buffers, DSQ_STAGES - 1 of them in
+// flight: the K tile (swizzled) and the 16 dS chunks of 1 KiB (four per
+// 32-query block), copied unchanged by direct global -> LDS loads spread
+// evenly over the waves.  Transposing reads turn the chunks into the
+// MFMA's B operand (one query per lane, eight keys).  Eight waves, two per
+// SIMD: wave w takes the 32 queries of block w % 4 and half of the head
+// width, so one wave's MFMAs run while the other waits on its LDS reads.
+constexpr int DSQ_STAGES = 4;
+constexpr int DSQ_WAVES = 8;
+constexpr int DSQ_THREADS = 64 * DSQ_WAVES;
+
+template <int D>
+__global__ __launch_bounds__(DSQ_THREADS, 1) void s2a_bwd_dq_ds_kernel(
+    const bf16_t *__restrict__ k, float *__restrict__ dq, S2AParams p) {
+  using T = SwTile<D>;
+  using LD = TileLoader<D, DQ_BK, DSQ_WAVES>;
+  constexpr int DB = D / 32, DBW = DB / 2;  // d-blocks per head, per wave
+  constexpr int TILEB = DQ_BK * T::ROWB;
+  constexpr int QBS = 4 * 1024;             // dS bytes per 32-query block
+  constexpr int STAGEB = TILEB + 4 * QBS;
+  constexpr int LPS = LD::IPW + 2;          // loads per wave and stage
+  static_assert((DSQ_STAGES - 2) * LPS < 64, "vmcnt range");
+  static_assert(DQ_BQ == 128 && DQ_BK == 64, "four 32-query blocks, 64 keys");
+  __shared__ __attribute__((aligned(1024))) char smem[DSQ_STAGES * STAGEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+
+  const UnitTile ut = decode(p, true);
+  if (!ut.ok) return;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
+  const int j = ut.tile;  // query tile; key block j holds its diagonal
+  const int q0 = j * DQ_BQ;
+  if (q0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const bf16_t *kbh = k + boff;
+  const int nkb = ds_nkb(p.g.G);
+  const char *dsw = (const char *)p.dsws;
+
+  // compute role: 32-query block wq (query tile 2j + wq/2, block wq%2 of
+  // it) and d-blocks DBW*dh .. DBW*dh + DBW - 1
+  const int wq = w & 3, dh = w >> 2;
+  const int qslot = q0 + 32 * wq + l32;
+  const int qp0 = qslot < glen ? run.pos(qslot) : -1;
+  const bool qin = qp0 >= 0;
+  const int qpos = qin ? qp0 : 0;
+  const bool qvalid = qin && qpos < L;
+  // load role: chunks 2 (w % 2) and 2 (w % 2) + 1 of 32-query block w / 2
+  const int lq = w >> 1, lqt = 2 * j + (lq >> 1), lqb = lq & 1;
+
+  LD ld;
+  ld.init(w, lane);
+  ld.init_rs(rs);
+  // Stage it < 2 (j + 1): keys 64 (it % 2) .. + 63 of key block it / 2;
+  // tile 0 has two more: the two halves of block 0 again, with the
+  // residual blocks.
+  const int nmain = 2 * (j + 1), nst = nmain + (j == 0 ? 2 : 0);
+  auto issue = [&](int it, int buf) {
+    const bool res = it >= nmain;
+    const int kb = res ? 0 : it >> 1, h = it & 1;
+    const int k0 = kb * KV_BK + h * DQ_BK;
+    char *kd = smem + buf * STAGEB;
+    if (tile_plain(run, glen, k0, DQ_BK, L))
+      ld.fast_s(kbh + (size_t)run.pos(k0) * rs, kd);
+    else
+      ld.general(kbh, rs, run, glen, k0, L, kd);
+    const size_t blk = res ? ds_res_block(ut.u, nkb, lq >> 1)
+                           : ds_block(ut.u, nkb, kb, lqt);
+    const char *src = dsw + blk * DS_BLOCK;
+    char *dd = kd + TILEB + lq * QBS;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      // chunk c (wave 2h + c/2 of dK/dV, block lqb, h2 = c%2)
+      const int c = 2 * (w & 1) + cc;
+      g2lds16_s(src + (((2 * h + (c >> 1)) * 2 + lqb) * 2 + (c & 1)) * 1024,
+                lane * 16, dd + c * 1024);
+    }
+  };
+
+  // K^T operand (A): transposing reads of rows trow, trow + 8 of a 16-row
+  // step, as in the other kernels.
+  int troff[DBW], troff8[DBW];
+#pragma unroll
+  for (int i = 0; i < DBW; ++i) {
+    const int db = DBW * dh + i;
+    const int c = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
+    troff[i] = T::off(trow, c) + (lane & 1) * 8;
+    troff8[i] = T::off(trow + 8, c) + (lane & 1) * 8;
+  }
+  // dS^T operand (B): in each group of 16 lanes, lane (r, pc) =
+  // ((lane >> 2) & 3, lane & 3) supplies the four dS of key
+  // 16 (s % 2) + 8 rd + 4 hf + r (s: the 16-key step, rd: the two reads)
+  // against queries 16 h2 + 4 pc .. 4 pc + 3 (h2 = grp % 2), and receives
+  // column 16 h2 + (lane & 15), its own query, for rows r = 0 .. 3.
+  int soff[2][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int a = lane & 1, h2 = grp & 1, r = (lane >> 2) & 3;
+      const int key = 16 * e + 8 * rd + 4 * hf + r;
+      soff[e][rd] = h2 * 1024 + 16 * ds_slot(a, key, h2) + 8 * ((lane >> 1) & 1);
+    }
+
+  f32x16 dqacc[DBW];
+#pragma unroll
+  for (int i = 0; i < DBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqacc[i][e] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < DSQ_STAGES - 1; ++s)
+    if (s < nst) issue(s, s);
+  for (int it = 0; it < nst; ++it) {
+    // stage it has landed once at most DSQ_STAGES - 2 later stages are
+    // outstanding (fewer near the end: then wait for everything)
+    if (it + DSQ_STAGES - 2 < nst) wait_vm<(DSQ_STAGES - 2) * LPS>();
+    else wait_vm_all();
+    // (also: every wave is done with the buffer of stage it - 1)
+    __syncthreads();
+    if (it + DSQ_STAGES - 1 < nst)
+      issue(it + DSQ_STAGES - 1, (it + DSQ_STAGES - 1) % DSQ_STAGES);
+    const char *Kb = smem + (it % DSQ_STAGES) * STAGEB;
+    const char *Sb = Kb + TILEB + wq * QBS;
+#pragma unroll
+    for (int s = 0; s < DQ_BK / 16; ++s) {
+      const char *sc = Sb + (s >> 1) * 2048;
+      const bf16x8 bs = cat4(lds_read_tr((const bf16_t *)(sc + soff[s & 1][0])),
+                             lds_read_tr((const bf16_t *)(sc + soff[s & 1][1])));
+      const char *kr = Kb + 16 * s * T::ROWB;
+#pragma unroll
+      for (int i = 0; i < DBW; ++i) {
+        const bf16x8 ak = cat4(lds_read_tr((const bf16_t *)(kr + troff[i])),
+                               lds_read_tr((const bf16_t *)(kr + troff8[i])));
+        dqacc[i] = mfma32(ak, bs, dqacc[i]);
+      }
+    }
+  }
+
+  if (qin) {
+    const size_t row = boff + (size_t)qpos * rs;
+#pragma unroll
+    for (int i = 0; i < DBW; ++i)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * (DBW * dh + i) + 8 * i4 + 4 * hf;
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
+        if (qvalid) {
+          val[0] = dqacc[i][4 * i4] * p.scale;
+          val[1] = dqacc[i][4 * i4 + 1] * p.scale;
+          val[2] = dqacc[i][4 * i4 + 2] * p.scale;
+          val[3] = dqacc[i][4 * i4 + 3] * p.scale;
+        }
+        *(f32x4 *)(dq + row + d) = val;
       }
   }
 }
@@ -1524,7 +1766,7 @@ dim3 unit_grid(const S2AParams &p, int rows_per_wg) {
   return dim3((unsigned)units_pad * (unsigned)tiles);
 }
 
-template <int D, bool DOC>
+template <int D, bool DOC, bool DS>
 hipError_t launch_dkdv_d(const void *q, const void *k, const void *v,
                          const void *dout, const float *lse,
                          const float *delta, float *dk, float *dv,
@@ -1537,7 +1779,7 @@ hipError_t launch_dkdv_d(const void *q, const void *k, const void *v,
                   (void *)&p};
   const void *fn;
   if constexpr (D >= 64)
-    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, DOC>;
+    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, DOC, DS>;
   else
     fn = (const void *)s2a_bwd_dkdv_kernel<D, DOC>;
   hipError_t e = hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
@@ -1562,8 +1804,11 @@ hipError_t launch_dkdv_t(const void *q, const void *k, const void *v,
                          const void *dout, const float *lse,
                          const float *delta, float *dk, float *dv,
                          const S2AParams &p, hipStream_t st) {
-  return p.doc ? launch_dkdv_d<D, true>(q, k, v, dout, lse, delta, dk, dv, p, st)
-               : launch_dkdv_d<D, false>(q, k, v, dout, lse, delta, dk, dv, p, st);
+  if constexpr (D >= 64)
+    if (p.dsws)  // (the host never pairs it with a document mask)
+      return launch_dkdv_d<D, false, true>(q, k, v, dout, lse, delta, dk, dv, p, st);
+  return p.doc ? launch_dkdv_d<D, true, false>(q, k, v, dout, lse, delta, dk, dv, p, st)
+               : launch_dkdv_d<D, false, false>(q, k, v, dout, lse, delta, dk, dv, p, st);
 }
 
 template <int D, bool DOC>
@@ -1584,14 +1829,30 @@ hipError_t launch_dq_d(const void *q, const void *k, const void *v,
 }
 
 template <int D>
+hipError_t launch_dq_ds(const void *k, float *dq, S2AParams p, hipStream_t st) {
+  p.tiles = (p.g.G + DQ_BQ - 1) / DQ_BQ;
+  const bf16_t *kk = (const bf16_t *)k;
+  void *args[] = {(void *)&kk, (void *)&dq, (void *)&p};
+  return hipLaunchKernel((const void *)s2a_bwd_dq_ds_kernel<D>,
+                         unit_grid(p, DQ_BQ), dim3(DSQ_THREADS), args, 0, st);
+}
+
+template <int D>
 hipError_t launch_dq_t(const void *q, const void *k, const void *v,
                        const void *dout, const float *lse, const float *delta,
                        float *dq, const S2AParams &p, hipStream_t st) {
+  if constexpr (D >= 64)
+    if (p.dsws) return launch_dq_ds<D>(k, dq, p, st);
   return p.doc ? launch_dq_d<D, true>(q, k, v, dout, lse, delta, dq, p, st)
                : launch_dq_d<D, false>(q, k, v, dout, lse, delta, dq, p, st);
 }
 
 }  // namespace
+
+long double s2a_ds_workspace_bytes(const S2AParams &p) {
+  const long double nkb = ds_nkb(p.g.G);
+  return (long double)p.units * (nkb * (nkb + 1) + 2) * DS_BLOCK;
+}
 
 hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,
                               float *delta, int B, int N, int H, int D,

@@ -29,6 +29,9 @@ struct S2AParams {
   float scale;    // softmax scale
   float scale_log2;  // scale * log2(e)
   const int *doc; // document IDs [B, N] (nullptr: no document mask)
+  // dS workspace of the backward (nullptr: the dQ kernel recomputes S and
+  // dP; otherwise dK/dV stores bf16 dS blocks there and dQ reads them)
+  void *dsws;
 };
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (checked on

@@ -32,6 +32,10 @@ hipError_t s2a_launch_bwd_dq(const void *q, const void *k, const void *v,
                              const float *delta, float *dq, int D,
                              const S2AParams &p, hipStream_t st);
 
+// Bytes of the dS workspace for the launch geometry p (long double: the
+// caller checks the range before it forms a size_t).
+long double s2a_ds_workspace_bytes(const S2AParams &p);
+
 hipError_t s2a_launch_map(const S2AGeom &g, int *gid, int *slot, int *src,
                           hipStream_t st);
 

@@ -7,6 +7,7 @@ raise.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -124,6 +125,65 @@ def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
     return dq, dk, dv
 
 
+def ds_workspace_bytes(B: int, N: int, H: int, D: int, *, G: int,
+                       shift: int | None = None, boundary="wrap") -> int:
+    """Bytes of the dS workspace that bwd_ds needs (D in {64, 128})."""
+    shift = G // 2 if shift is None else shift
+    out = ctypes.c_size_t(0)
+    _lib.check(_lib.load().s2attn_bwd_ds_workspace(
+        B, N, H, D, G, shift, _boundary(boundary), ctypes.byref(out)))
+    return int(out.value)
+
+
+def ds_workspace(q, *, G: int, shift: int | None = None, boundary="wrap"):
+    """A device buffer for bwd_ds / bwd_dkdv_ds / bwd_dq_ds (uint8)."""
+    B, N, H, D = q.shape
+    n = ds_workspace_bytes(B, N, H, D, G=G, shift=shift, boundary=boundary)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def _ds_arg(ds_ws):
+    if ds_ws.dtype != torch.uint8 or ds_ws.dim() != 1 or not ds_ws.is_contiguous():
+        raise ValueError("ds_ws must be a contiguous 1-D uint8 tensor")
+    return ds_ws.data_ptr(), ds_ws.numel()
+
+
+def bwd_ds(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
+           boundary="wrap", valid_len: int | None = None,
+           scale: float | None = None, dq=None, dk=None, dv=None, delta=None,
+           ds_ws=None):
+    """The backward that stores dS in a workspace (dK/dV) and reads it for
+    dQ instead of recomputing S and dP.  D in {64, 128}, no document mask.
+    Returns (dq, dk, dv), float32 [B,N,H,D]."""
+    B, N, H, D = _check_qkv(q, k, v, dout)
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
+            or not o.is_contiguous():
+        raise ValueError("o must be a contiguous [B,N,H,D] float32/bfloat16 tensor")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
+    mk = lambda: torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous float32 [B,N,H,D]")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if ds_ws is None:
+        ds_ws = ds_workspace(q, G=G, shift=shift, boundary=boundary)
+    wp, wn = _ds_arg(ds_ws)
+    odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
+    _lib.check(_lib.load().s2attn_bwd_ds(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), odt, _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), wp, wn, B, N, H, D, G,
+        shift, _boundary(boundary), valid_len, scale, _stream(q.device)))
+    return dq, dk, dv
+
+
 def bwd_preprocess(o, dout, delta):
     """First backward stage: delta = rowsum(dout * o)."""
     B, N, H, D = _check_qkv(dout)
@@ -172,6 +232,31 @@ def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
                                  _ptr(delta), _ptr(dout), _ptr(dq), B, N, H,
                                  D, G, shift, _boundary(boundary), valid_len,
                                  _docs(doc_ids, q), scale, _stream(q.device)))
+
+
+def bwd_dkdv_ds(q, k, v, lse, delta, dout, dk, dv, ds_ws, *, G: int,
+                shift: int | None = None, boundary="wrap",
+                valid_len: int | None = None, scale: float | None = None):
+    """The dK/dV stage of bwd_ds (fills ds_ws); for timing one kernel."""
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
+                                                         valid_len, scale)
+    wp, wn = _ds_arg(ds_ws)
+    _lib.check(_lib.load().s2attn_bwd_dkdv_ds(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(dout),
+        _ptr(dk), _ptr(dv), wp, wn, B, N, H, D, G, shift, _boundary(boundary),
+        valid_len, scale, _stream(q.device)))
+
+
+def bwd_dq_ds(k, ds_ws, dq, *, G: int, shift: int | None = None,
+              boundary="wrap", valid_len: int | None = None,
+              scale: float | None = None):
+    """The dQ stage of bwd_ds: dq from the dS that bwd_dkdv_ds stored."""
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(k, G, shift,
+                                                         valid_len, scale)
+    wp, wn = _ds_arg(ds_ws)
+    _lib.check(_lib.load().s2attn_bwd_dq_ds(
+        _ptr(k), wp, wn, _ptr(dq), B, N, H, D, G, shift, _boundary(boundary),
+        valid_len, scale, _stream(k.device)))
 
 
 def shard_halo(N: int, row0: int, T: int, *, G: int, shift: int | None = None,

@@ -90,6 +90,56 @@ def test_misaligned_pointer_rejected():
     assert st == _lib.S2A_EINVAL
 
 
+def test_stored_ds_workspace_size():
+    # blocks of 64 queries x 128 keys (16 KiB), nkb (nkb + 1) + 2 per unit
+    # with nkb = ceil(G / 128): the causal blocks plus two residual blocks
+    # of key block 0; units = B * H * (groups of the larger class)
+    lib = _lib.load()
+    out = ctypes.c_size_t(0)
+    for (B, N, H, D, G, bnd, groups) in [(1, 32768, 32, 128, 8192, 0, 4),
+                                         (2, 12288, 32, 64, 1536, 1, 9),
+                                         (1, 1024, 2, 128, 1024, 2, 1),
+                                         (1, 192, 2, 128, 96, 0, 2)]:
+        assert lib.s2attn_bwd_ds_workspace(B, N, H, D, G, G // 2, bnd,
+                                           ctypes.byref(out)) == _lib.S2A_OK
+        nkb = -(-G // 128)
+        assert out.value == B * H * groups * (nkb * (nkb + 1) + 2) * 16384
+    assert lib.s2attn_bwd_ds_workspace(1, 64, 4, 32, 16, 8, 0,
+                                       ctypes.byref(out)) == _lib.S2A_EUNSUPPORTED
+    assert lib.s2attn_bwd_ds_workspace(1, 64, 4, 64, 16, 8, 0,
+                                       None) == _lib.S2A_EINVAL
+    assert lib.s2attn_bwd_ds_workspace(1, 60, 4, 64, 16, 8, 0,
+                                       ctypes.byref(out)) == _lib.S2A_EINVAL
+
+
+def test_stored_ds_rejects_bad_workspace_before_launch():
+    lib = _lib.load()
+    buf = (ctypes.c_char * 4096)()
+    p = ((ctypes.addressof(buf) + 15) // 16) * 16
+    out = ctypes.c_size_t(0)
+    lib.s2attn_bwd_ds_workspace(1, 256, 2, 128, 64, 32, 0, ctypes.byref(out))
+    need = out.value
+
+    def ds(ws, nbytes, D=128):
+        return lib.s2attn_bwd_ds(p, p, p, p, 1, p, p, p, p, p, p, ws, nbytes,
+                                 1, 256, 2, D, 64, 32, 0, 256, 0.1, None)
+
+    def dkdv(ws, nbytes, D=128):
+        return lib.s2attn_bwd_dkdv_ds(p, p, p, p, p, p, p, p, ws, nbytes, 1,
+                                      256, 2, D, 64, 32, 0, 256, 0.1, None)
+
+    def dq(ws, nbytes, D=128):
+        return lib.s2attn_bwd_dq_ds(p, ws, nbytes, p, 1, 256, 2, D, 64, 32, 0,
+                                    256, 0.1, None)
+
+    for call in (ds, dkdv, dq):
+        assert call(None, need) == _lib.S2A_EINVAL
+        assert call(p + 8, need) == _lib.S2A_EINVAL          # misaligned
+        assert call(p, need - 1) == _lib.S2A_EINVAL          # too short
+        assert "workspace" in lib.s2attn_last_error().decode()
+        assert call(p, need, D=32) == _lib.S2A_EUNSUPPORTED
+
+
 def test_rope_rejects_bad_arguments():
     lib = _lib.load()
     buf = (ctypes.c_char * 4096)()

@@ -74,13 +74,14 @@ def sample_rows(N, G, shift, boundary, L, cls, doc=None):
 
 
 def check_workload(config, variant, B, N, H, D, G, boundary, L, with_bwd,
-                   doc=None):
+                   doc=None, ds=False):
     shift = G // 2
     sc = scale_for(D)
     heads = [1, H - 2]             # one head of each class
     say(f"config {config} B={B} N={N} H={H} D={D} G={G} L={L} "
         f"boundary={boundary} bwd={with_bwd} "
-        f"documents={None if doc is None else int(doc.max()) + 1}")
+        f"documents={None if doc is None else int(doc.max()) + 1} "
+        f"stored_ds={ds}")
     dev, host = gen(config, variant, B, N, H, D, L, heads, with_bwd)
     dd = None if doc is None else torch.from_numpy(doc).cuda()
     o, lse = s2a.fwd(dev["q"], dev["k"], dev["v"], G=G, shift=shift,
@@ -89,6 +90,18 @@ def check_workload(config, variant, B, N, H, D, G, boundary, L, with_bwd,
         dq, dk, dv = s2a.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"],
                              G=G, shift=shift, boundary=boundary,
                              valid_len=L, scale=sc, doc_ids=dd)
+    if with_bwd and ds:
+        # the stored-dS backward: dk, dv bit for bit those of the
+        # recompute path, dq checked against the oracle below
+        dq0, dk0, dv0 = dq, dk, dv
+        dq, dk, dv = s2a.bwd_ds(dev["q"], dev["k"], dev["v"], o, lse,
+                                dev["do"], G=G, shift=shift,
+                                boundary=boundary, valid_len=L, scale=sc)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, dk0) and torch.equal(dv, dv0)
+        say(f"  dq vs recompute path: max|d|="
+            f"{(dq - dq0).abs().max().item():.3e}")
+        del dq0, dk0, dv0
     torch.cuda.synchronize()
     # padded rows are exactly zero everywhere (cheap to check in full)
     if L < N:
@@ -161,6 +174,23 @@ def test_headline_shape_cyclic_32k():
 def test_ragged_100k(boundary):
     check_workload(5, boundary, 1, 102400, 32, 128, 25600, boundary, 100000,
                    True)
+
+
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.CYCLIC])
+def test_headline_stored_ds_32k(boundary):
+    check_workload(3, boundary, 1, 32768, 32, 128, 8192, boundary, 32768,
+                   True, ds=True)
+
+
+def test_ratio_sweep_stored_ds_smallest_group():
+    check_workload(4, 4, 2, 12288, 32, 128, 1536, syn.SPLIT, 12288, True,
+                   ds=True)
+
+
+@pytest.mark.parametrize("boundary", [syn.WRAP, syn.CYCLIC])
+def test_ragged_100k_stored_ds(boundary):
+    check_workload(5, boundary, 1, 102400, 32, 128, 25600, boundary, 100000,
+                   True, ds=True)
 
 
 @pytest.mark.parametrize("boundary", [syn.WRAP, syn.CYCLIC])
