@@ -150,8 +150,9 @@ SWEEP_GS = (12288, 6144, 3072, 2048, 1536)
 
 def sweep(args):
     """Shift ablation over the group-ratio sweep: the same step (forward,
-    preprocess, dK/dV, dQ) timed with HIP events for shift 0 (plain
-    grouping) and shift G/2 under each boundary variant."""
+    preprocess, dK/dV, dQ; the stored-dS backward unless --recompute-dq)
+    timed with HIP events for shift 0 (plain grouping) and shift G/2 under
+    each boundary variant."""
     import torch
     import synthetic as syn
     import sparse_attention_long_attn_amd as s2a
@@ -173,12 +174,18 @@ def sweep(args):
         for shift, bnd in ((0, syn.SPLIT), (G // 2, syn.SPLIT),
                            (G // 2, syn.WRAP), (G // 2, syn.CYCLIC)):
             kw = dict(G=G, shift=shift, boundary=bnd, valid_len=N)
+            ws = None if args.recompute_dq else s2a.ds_workspace(
+                q, G=G, shift=shift, boundary=bnd)
 
             def step():
                 s2a.fwd(q, k, v, o=o, lse=lse, **kw)
                 s2a.bwd_preprocess(o, do, delta)
-                s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
-                s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+                if ws is None:
+                    s2a.bwd_dkdv(q, k, v, lse, delta, do, dk, dv, **kw)
+                    s2a.bwd_dq(q, k, v, lse, delta, do, dq, **kw)
+                else:
+                    s2a.bwd_dkdv_ds(q, k, v, lse, delta, do, dk, dv, ws, **kw)
+                    s2a.bwd_dq_ds(k, ws, dq, **kw)
 
             for _ in range(args.warmup):
                 step()
@@ -198,6 +205,8 @@ def sweep(args):
                 "value": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 2),
                 "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
                 "steps": args.steps, "warmup": args.warmup,
+                "backward": "recomputed S, dP for dQ" if ws is None
+                            else "stored dS",
                 "config": {"workload": f"B={B} N={N} H={H} D={D} G={G} "
                                        f"shift={shift} {names[bnd]}",
                            "group": G, "shift": shift,
@@ -205,6 +214,8 @@ def sweep(args):
                            "ratio_to_full_causal": round(
                                pairs / (B * H * N * (N + 1) / 2), 4)},
             }), flush=True)
+            del ws
+            torch.cuda.empty_cache()
 
 
 def rope_bench(args):
