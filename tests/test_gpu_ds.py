@@ -31,6 +31,9 @@ CASES = [
     (1, 256, 2, 64, 64, 256, 1),       # half groups of 32 slots
     (1, 8, 2, 64, 4, 5, 1),            # the N=8, G=4 worked example, padded
     (1, 8192, 2, 128, 2048, 8000, 1),  # many key blocks per group, padded
+    (1, 16, 2, 64, 2, 13, 1),          # groups of two tokens (s = 1)
+    (2, 64, 4, 64, 32, 50, 0),         # shift 0, padded, B = 2
+    (1, 384, 2, 128, 384, 200, 1),     # G = N (no shift), half padded
 ]
 
 
