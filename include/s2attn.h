@@ -158,7 +158,9 @@ s2a_status s2attn_bwd_dq(const void *q, const void *k, const void *v,
  *
  * ds_ws: device workspace of at least s2attn_bwd_ds_workspace() bytes,
  * 16-byte aligned, owned by the caller; its contents are scratch (written
- * by the dK/dV stage, read by the dQ stage; neither zeroes it first).
+ * by the dK/dV stage, read by the dQ stage; neither zeroes it first, and
+ * no output depends on bytes the dK/dV stage did not write).  Calls that
+ * may run at the same time (other streams) need workspaces of their own.
  * About 2 bytes per allowed pair: 8.7 GB for B=1, N=32768, H=32, G=8192.
  * Other arguments as for s2attn_bwd.  Errors: S2A_EUNSUPPORTED for other
  * D, S2A_EINVAL for a missing, misaligned or short workspace, as well as
