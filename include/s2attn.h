@@ -197,8 +197,12 @@ s2a_status s2attn_bwd_dq_ds(const void *k, const void *ds_ws,
 
 /*
  * Group index maps, computed on the device by the same group geometry the
- * attention kernels use.  For head class c (0: heads < H/2, 1: the rest)
- * and original position x:
+ * attention kernels use (PaperTrace "4.1.2 · LongLoRA", §1: the group
+ * functions b(i) = floor(i/G) of the unshifted heads and
+ * b'(i) = floor((i - G/2)/G) of the shifted ones, the N=8, G=4 worked
+ * example, and the cyclic-shift paragraph for the boundary variants; §2.2
+ * for the cyclic-causal partition).  For head class c (0: heads < H/2,
+ * 1: the rest) and original position x:
  *   gid[c*N + x]  = group of x,   slot[c*N + x] = rank of x in its group,
  * and for row r of the regrouped layout (groups laid end to end in order):
  *   src[c*N + r]  = original position held at row r.

@@ -5,7 +5,7 @@
 Compiles every .hip source under csrc/ with hipcc for --offload-arch=gfx950
 and links them into sparse_attention_long_attn_amd/libs2attn.so.  Packed
 fp32 instructions are disabled on the device side (a known-unreliable form
-on these parts); fp32 atomics use the hardware instructions.
+on these parts).  The library uses no atomics.
 """
 from __future__ import annotations
 
@@ -21,7 +21,6 @@ ROOT = os.path.dirname(PKG)
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-    "-munsafe-fp-atomics",
     # MFMA results in VGPRs by default (long-lived accumulators are pinned
     # to AGPRs explicitly where wanted); avoids AGPR<->VGPR copies
     "-mllvm", "-amdgpu-mfma-vgpr-form",

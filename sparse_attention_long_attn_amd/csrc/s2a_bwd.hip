@@ -4,29 +4,34 @@
 // "4.1.2 · LongLoRA: 用S²-Attn完成长上下文微调", §3) and stay inside each
 // group: no out-of-group pair is ever visited (§1.1, "反向传播确实保持稀疏").
 //
-// Three kernels, none using atomics:
+// Kernels, none using atomics:
 //   s2a_bwd_pre_kernel   delta_x = dO_x . O_x per (batch, head, row)
-//   s2a_bwd_dkdv_kernel  one workgroup owns 128 keys of one group and walks
+//   s2a_bwd_dkdv_kernel / s2a_bwd_dkdv_sw_kernel (D < 64 / D >= 64)
+//                        one workgroup owns 128 keys of one group and walks
 //                        the group's query tiles at or after them:
 //                          S = Q K^T, dP = dO V^T         (K, V in registers)
 //                          P = exp(S - lse), dS = P (dP - delta)
 //                          dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T through
 //                                                          transposing LDS reads)
-//                        and stores dK, dV once at the end;
-//   s2a_bwd_dq_kernel    one workgroup owns 128 queries of one group and
+//                        and stores dK, dV once at the end; its DS variant
+//                        also stores bf16 dS to a workspace;
+//   s2a_bwd_dq_kernel / s2a_bwd_dq_sw_kernel
+//                        one workgroup owns 128 queries of one group and
 //                        walks the group's key tiles up to them, in the
 //                        forward's orientation (one query per lane column):
 //                          S^T = K Q^T, dP^T = V dO^T, dS^T as above,
 //                          dQ^T += K^T dS^T
 //                        and stores dQ once at the end;
+//   s2a_bwd_dq_ds_kernel dQ^T += K^T dS^T from the stored dS (nothing
+//                        recomputed);
 //   s2a_bwd_dkdv_lo_kernel (D >= 64) adds the bf16 rounding residuals of P
 //                        and dS of "hot" query tiles (queries that see few
 //                        keys) to dK and dV.
 // Under a document mask (packed sequences) a pair also needs equal document
 // IDs, in both head classes (PaperTrace 4.1.2, §1.1, the paragraph on
 // causal masks and sample packing).
-// Splitting dQ off costs 4*D extra MFMA work per pair (S and dP are
-// recomputed) but replaces fp32 atomics whose traffic (one read-modify-
+// Splitting dQ off costs either 4*D extra MFMA work per pair (S and dP
+// recomputed) or 2 bytes of stored dS per pair, but replaces fp32 atomics whose traffic (one read-modify-
 // write of a 64x128 fp32 tile per key tile and query tile) cost more than
 // the whole rest of the backward.
 #include <type_traits>

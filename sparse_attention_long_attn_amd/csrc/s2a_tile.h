@@ -9,12 +9,11 @@
 // that fills physical chunk p of row r therefore reads logical chunk
 // p ^ swz(r) from global memory.
 //
-// swz(r) = 2*(r mod 8) + (r/8 mod 2) serves both read patterns of the
-// kernels at full rate on gfx950 (measured, D = 128): 16-byte operand reads
-// (32 lanes on 32 consecutive rows, same chunk) at ~245 B/clk per CU, and
-// ds_read_b64_tr_b16 (16 lanes on 4 consecutive rows, 2 adjacent chunks
-// each; the xor keeps a chunk pair together) at ~122 B/clk per CU.  An
-// unpermuted layout gets 16 and 64 B/clk respectively.
+// swz(r) (see SwTile below) is chosen so that both read patterns of the
+// kernels touch every LDS bank once per pass: 16-byte operand reads (32
+// lanes on 32 consecutive rows, same logical chunk) and ds_read_b64_tr_b16
+// (16 lanes on 4 consecutive rows, chunks 4j .. 4j+3).  An unpermuted
+// layout serialises both on a few banks.
 #pragma once
 #include <limits.h>
 #include <stdint.h>

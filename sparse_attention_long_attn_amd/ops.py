@@ -47,6 +47,21 @@ def _check_qkv(*ts, shape=None):
     return shape
 
 
+def _need(t, shape, dtypes, dev, name):
+    """Raise ValueError unless ``t`` is a contiguous tensor of ``shape``,
+    one of ``dtypes``, on device ``dev`` (checked before any launch: a
+    pointer to host memory handed to a kernel faults the GPU)."""
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes \
+            or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != dev:
+        names = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be a contiguous {names} "
+                         f"{tuple(shape)} tensor on {dev}")
+    return t
+
+
 def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -78,10 +93,8 @@ def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
         o = torch.empty((B, N, H, D), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if o.dtype != out_dtype or o.shape != q.shape or not o.is_contiguous():
-        raise ValueError("o must be a contiguous [B,N,H,D] tensor of out_dtype")
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
+    _need(o, q.shape, out_dtype, q.device, "o")
+    _need(lse, (B, H, N), torch.float32, q.device, "lse")
     odt = _lib.S2A_F32 if out_dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()
     _lib.check(lib.s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
@@ -89,6 +102,23 @@ def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
                               _boundary(boundary), valid_len,
                               _docs(doc_ids, q), scale, _stream(q.device)))
     return o, lse
+
+
+def _bwd_tensors(q, o, lse, dq, dk, dv, delta):
+    """Check the forward's outputs and the backward's outputs and Δ
+    workspace (allocated when None) against q's shape and device."""
+    B, N, H, D = q.shape
+    f32, dev = torch.float32, q.device
+    _need(o, q.shape, (f32, torch.bfloat16), dev, "o")
+    _need(lse, (B, H, N), f32, dev, "lse")
+    mk = lambda: torch.empty((B, N, H, D), dtype=f32, device=dev)
+    dq = _need(mk() if dq is None else dq, q.shape, f32, dev, "dq")
+    dk = _need(mk() if dk is None else dk, q.shape, f32, dev, "dk")
+    dv = _need(mk() if dv is None else dv, q.shape, f32, dev, "dv")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=f32, device=dev)
+    _need(delta, (B, H, N), f32, dev, "delta")
+    return dq, dk, dv, delta
 
 
 def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
@@ -101,20 +131,7 @@ def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
     shift = G // 2 if shift is None else shift
     valid_len = N if valid_len is None else valid_len
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
-            or not o.is_contiguous():
-        raise ValueError("o must be a contiguous [B,N,H,D] float32/bfloat16 tensor")
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
-    mk = lambda: torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
-    dq = mk() if dq is None else dq
-    dk = mk() if dk is None else dk
-    dv = mk() if dv is None else dv
-    for t in (dq, dk, dv):
-        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous float32 [B,N,H,D]")
-    if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv, delta = _bwd_tensors(q, o, lse, dq, dk, dv, delta)
     odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()
     _lib.check(lib.s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), odt,
@@ -142,9 +159,12 @@ def ds_workspace(q, *, G: int, shift: int | None = None, boundary="wrap"):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
 
 
-def _ds_arg(ds_ws):
-    if ds_ws.dtype != torch.uint8 or ds_ws.dim() != 1 or not ds_ws.is_contiguous():
-        raise ValueError("ds_ws must be a contiguous 1-D uint8 tensor")
+def _ds_arg(ds_ws, dev):
+    if not isinstance(ds_ws, torch.Tensor) or ds_ws.dtype != torch.uint8 \
+            or ds_ws.dim() != 1 or not ds_ws.is_contiguous() \
+            or ds_ws.device != dev:
+        raise ValueError(f"ds_ws must be a contiguous 1-D uint8 tensor on "
+                         f"{dev}")
     return ds_ws.data_ptr(), ds_ws.numel()
 
 
@@ -159,23 +179,10 @@ def bwd_ds(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
     shift = G // 2 if shift is None else shift
     valid_len = N if valid_len is None else valid_len
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
-            or not o.is_contiguous():
-        raise ValueError("o must be a contiguous [B,N,H,D] float32/bfloat16 tensor")
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor")
-    mk = lambda: torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
-    dq = mk() if dq is None else dq
-    dk = mk() if dk is None else dk
-    dv = mk() if dv is None else dv
-    for t in (dq, dk, dv):
-        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous float32 [B,N,H,D]")
-    if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv, delta = _bwd_tensors(q, o, lse, dq, dk, dv, delta)
     if ds_ws is None:
         ds_ws = ds_workspace(q, G=G, shift=shift, boundary=boundary)
-    wp, wn = _ds_arg(ds_ws)
+    wp, wn = _ds_arg(ds_ws, q.device)
     odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
     _lib.check(_lib.load().s2attn_bwd_ds(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), odt, _ptr(lse), _ptr(dout),
@@ -187,6 +194,8 @@ def bwd_ds(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
 def bwd_preprocess(o, dout, delta):
     """First backward stage: delta = rowsum(dout * o)."""
     B, N, H, D = _check_qkv(dout)
+    _need(o, dout.shape, (torch.float32, torch.bfloat16), dout.device, "o")
+    _need(delta, (B, H, N), torch.float32, dout.device, "delta")
     odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
     lib = _lib.load()
     _lib.check(lib.s2attn_bwd_preprocess(_ptr(o), odt, _ptr(dout),
@@ -194,8 +203,16 @@ def bwd_preprocess(o, dout, delta):
                                          _stream(dout.device)))
 
 
-def _stage_args(q, G, shift, valid_len, scale):
+def _stage_args(q, G, shift, valid_len, scale, lse=None, delta=None,
+                outs=()):
+    """Defaults of a stage call, after checking its statistics (lse,
+    delta: float32 [B,H,N]) and its float32 [B,N,H,D] outputs."""
     B, N, H, D = q.shape
+    for t, name in ((lse, "lse"), (delta, "delta")):
+        if t is not None:
+            _need(t, (B, H, N), torch.float32, q.device, name)
+    for t, name in outs:
+        _need(t, q.shape, torch.float32, q.device, name)
     shift = G // 2 if shift is None else shift
     valid_len = N if valid_len is None else valid_len
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -208,8 +225,8 @@ def bwd_dkdv(q, k, v, lse, delta, dout, dk, dv, *, G: int,
              doc_ids=None):
     """dK/dV stage (needs delta from bwd_preprocess)."""
     _check_qkv(q, k, v, dout)
-    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
-                                                         valid_len, scale)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(
+        q, G, shift, valid_len, scale, lse, delta, ((dk, "dk"), (dv, "dv")))
     lib = _lib.load()
     _lib.check(lib.s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
                                    _ptr(delta), _ptr(dout), _ptr(dk),
@@ -225,8 +242,8 @@ def bwd_dq(q, k, v, lse, delta, dout, dq, *, G: int,
            doc_ids=None):
     """dQ stage (needs delta from bwd_preprocess)."""
     _check_qkv(q, k, v, dout)
-    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
-                                                         valid_len, scale)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(
+        q, G, shift, valid_len, scale, lse, delta, ((dq, "dq"),))
     lib = _lib.load()
     _lib.check(lib.s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse),
                                  _ptr(delta), _ptr(dout), _ptr(dq), B, N, H,
@@ -238,9 +255,10 @@ def bwd_dkdv_ds(q, k, v, lse, delta, dout, dk, dv, ds_ws, *, G: int,
                 shift: int | None = None, boundary="wrap",
                 valid_len: int | None = None, scale: float | None = None):
     """The dK/dV stage of bwd_ds (fills ds_ws); for timing one kernel."""
-    B, N, H, D, G, shift, valid_len, scale = _stage_args(q, G, shift,
-                                                         valid_len, scale)
-    wp, wn = _ds_arg(ds_ws)
+    _check_qkv(q, k, v, dout)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(
+        q, G, shift, valid_len, scale, lse, delta, ((dk, "dk"), (dv, "dv")))
+    wp, wn = _ds_arg(ds_ws, q.device)
     _lib.check(_lib.load().s2attn_bwd_dkdv_ds(
         _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(delta), _ptr(dout),
         _ptr(dk), _ptr(dv), wp, wn, B, N, H, D, G, shift, _boundary(boundary),
@@ -251,9 +269,10 @@ def bwd_dq_ds(k, ds_ws, dq, *, G: int, shift: int | None = None,
               boundary="wrap", valid_len: int | None = None,
               scale: float | None = None):
     """The dQ stage of bwd_ds: dq from the dS that bwd_dkdv_ds stored."""
-    B, N, H, D, G, shift, valid_len, scale = _stage_args(k, G, shift,
-                                                         valid_len, scale)
-    wp, wn = _ds_arg(ds_ws)
+    _check_qkv(k)
+    B, N, H, D, G, shift, valid_len, scale = _stage_args(
+        k, G, shift, valid_len, scale, outs=((dq, "dq"),))
+    wp, wn = _ds_arg(ds_ws, k.device)
     _lib.check(_lib.load().s2attn_bwd_dq_ds(
         _ptr(k), wp, wn, _ptr(dq), B, N, H, D, G, shift, _boundary(boundary),
         valid_len, scale, _stream(k.device)))
@@ -316,11 +335,7 @@ def _out(t, shape, dtype, dev, name, zero=False):
     if t is None:
         return (torch.zeros if zero else torch.empty)(shape, dtype=dtype,
                                                       device=dev)
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) \
-            or not t.is_contiguous() or t.device != dev:
-        raise ValueError(f"{name} must be a contiguous {dtype} {tuple(shape)} "
-                         f"tensor on {dev}")
-    return t
+    return _need(t, shape, dtype, dev, name)
 
 
 def fwd_shard(q, k_ext, v_ext, *, N: int, row0: int, G: int,
@@ -360,16 +375,9 @@ def bwd_shard(q, k_ext, v_ext, o, lse, dout, *, N: int, row0: int, G: int,
     T, H, D, shift, valid_len, scale, R, kp, vp, doc = _shard_args(
         q, k_ext, v_ext, N, row0, G, shift, boundary, valid_len, scale,
         doc_ext)
-    if dout.shape != q.shape or dout.dtype != torch.bfloat16 \
-            or not dout.is_contiguous():
-        raise ValueError("dout must be a contiguous bfloat16 [T, H, D] tensor")
-    if o.shape != q.shape or o.dtype not in (torch.float32, torch.bfloat16) \
-            or not o.is_contiguous():
-        raise ValueError("o must be a contiguous [T, H, D] float32/bfloat16 "
-                         "tensor")
-    if lse.dtype != torch.float32 or lse.shape != (H, T) \
-            or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [H, T] tensor")
+    _need(dout, q.shape, torch.bfloat16, q.device, "dout")
+    _need(o, q.shape, (torch.float32, torch.bfloat16), q.device, "o")
+    _need(lse, (H, T), torch.float32, q.device, "lse")
     f32, dev = torch.float32, q.device
     dq = _out(dq, (T, H, D), f32, dev, "dq")
     dk = _out(dk, (R + T, H, D), f32, dev, "dk", zero=True)
@@ -420,8 +428,7 @@ def rope(x, *, base: float = 10000.0, pos_scale: float = 1.0, pos_ids=None,
         raise ValueError("x must be bfloat16")
     B, N, H, D, pp, pr = _rope_args(x, pos_ids, pairing)
     out = torch.empty_like(x) if out is None else out
-    if out.dtype != torch.bfloat16 or out.shape != x.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor like x")
+    _need(out, x.shape, torch.bfloat16, x.device, "out")
     lib = _lib.load()
     _lib.check(lib.s2attn_rope(_ptr(x), _ptr(out), B, N, H, D, pp, base,
                                pos_scale, pr, _stream(x.device)))
@@ -436,8 +443,7 @@ def rope_bwd(gy, *, base: float = 10000.0, pos_scale: float = 1.0,
         raise ValueError("gy must be float32")
     B, N, H, D, pp, pr = _rope_args(gy, pos_ids, pairing)
     out = torch.empty_like(gy) if out is None else out
-    if out.dtype != torch.float32 or out.shape != gy.shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor like gy")
+    _need(out, gy.shape, torch.float32, gy.device, "out")
     lib = _lib.load()
     _lib.check(lib.s2attn_rope_bwd(_ptr(gy), _ptr(out), B, N, H, D, pp, base,
                                    pos_scale, pr, _stream(gy.device)))

@@ -221,3 +221,28 @@ def test_work_pairs_of_the_headline_workload():
     assert c0 == c1 == 4 * 8192 * 8193 // 2
     fwd, bwd = work.useful_flops(1, 32768, 32, 128, 8192, 4096, 0, 32768)
     assert fwd == 4 * 128 * 16 * (c0 + c1) and bwd == 2.5 * fwd
+
+
+def test_torch_wrappers_reject_host_tensors():
+    # The torch layer refuses tensors in host memory with a ValueError
+    # before it reaches the library (no GPU is needed to see it).
+    import torch
+    from sparse_attention_long_attn_amd import ops
+    q = torch.zeros((1, 64, 2, 64), dtype=torch.bfloat16)
+    o = torch.zeros((1, 64, 2, 64), dtype=torch.float32)
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    for call in (lambda: ops.fwd(q, q, q, G=16),
+                 lambda: ops.bwd(q, q, q, o, lse, q, G=16),
+                 lambda: ops.bwd_dq_ds(q, ws, o, G=16),
+                 lambda: ops.bwd_dkdv_ds(q, q, q, lse, lse, q, o, o, ws,
+                                         G=16)):
+        with pytest.raises(ValueError):
+            call()
+    # the shared check names the argument, its shape and the device wanted
+    with pytest.raises(ValueError, match=r"dq must be a contiguous float32 "
+                                         r"\(1, 64, 2, 64\) tensor on cuda"):
+        ops._need(o, (1, 64, 2, 64), torch.float32, torch.device("cuda"),
+                  "dq")
+    with pytest.raises(ValueError, match="ds_ws"):
+        ops._ds_arg(ws, torch.device("cuda"))

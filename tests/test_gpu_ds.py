@@ -107,3 +107,47 @@ def test_stored_ds_rejects_what_it_does_not_cover():
         s2a.bwd_ds(q, q, q, o, lse, q, G=64, ds_ws=short, dq=dq)
     torch.cuda.synchronize()
     assert torch.all(dq == 7.0)  # nothing written
+
+
+def test_host_buffers_rejected_before_launch():
+    # Every tensor argument of the torch wrappers must sit on q's GPU: a
+    # host tensor (whose pointer a kernel would dereference) is a
+    # ValueError before anything is enqueued.
+    B, N, H, D, G = 1, 256, 2, 128, 64
+    dev = torch.device("cuda")
+    q = torch.zeros((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    o = torch.zeros((B, N, H, D), dtype=torch.float32, device=dev)
+    lse = torch.zeros((B, H, N), dtype=torch.float32, device=dev)
+    delta = torch.zeros((B, H, N), dtype=torch.float32, device=dev)
+    ws = s2a.ds_workspace(q, G=G)
+    cpu_ws = torch.empty(ws.numel(), dtype=torch.uint8)
+    cpu32 = torch.zeros((B, N, H, D), dtype=torch.float32)
+    cpu_stat = torch.zeros((B, H, N), dtype=torch.float32)
+    sentinel = [torch.full_like(o, 7.0) for _ in range(3)]
+    dq, dk, dv = sentinel
+    calls = [
+        lambda: s2a.bwd_ds(q, q, q, o, lse, q, G=G, ds_ws=cpu_ws, dq=dq,
+                           dk=dk, dv=dv),
+        lambda: s2a.bwd_dkdv_ds(q, q, q, lse, delta, q, dk, dv, cpu_ws, G=G),
+        lambda: s2a.bwd_dq_ds(q, cpu_ws, dq, G=G),
+        lambda: s2a.bwd_dq_ds(q, ws, cpu32, G=G),
+        lambda: s2a.bwd_dkdv_ds(q, q, q, lse, delta, q, cpu32, dv, ws, G=G),
+        lambda: s2a.bwd_dkdv_ds(q, q, q, cpu_stat, delta, q, dk, dv, ws,
+                                G=G),
+        lambda: s2a.bwd_dkdv(q, q, q, lse, cpu_stat, q, dk, dv, G=G),
+        lambda: s2a.bwd_dq(q, q, q, lse, delta, q, cpu32, G=G),
+        lambda: s2a.bwd(q, q, q, o, lse, q, G=G, dq=cpu32, dk=dk, dv=dv),
+        lambda: s2a.bwd(q, q, q, o, lse, q, G=G, dq=dq, dk=dk, dv=dv,
+                        delta=cpu_stat),
+        lambda: s2a.bwd(q, q, q, cpu32, lse, q, G=G, dq=dq, dk=dk, dv=dv),
+        lambda: s2a.bwd_preprocess(o, q, cpu_stat),
+        lambda: s2a.fwd(q, q, q, G=G, o=cpu32),
+        lambda: s2a.fwd(q, q, q, G=G, o=o, lse=cpu_stat),
+    ]
+    for i, call in enumerate(calls):
+        say(f"  host-buffer call {i}")
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+    for t in sentinel:
+        assert torch.all(t == 7.0)  # nothing was written
