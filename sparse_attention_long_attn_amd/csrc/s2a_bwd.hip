@@ -1315,9 +1315,17 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     }  // live
-    // the next step reads tile pre and its stats, both issued at the top
-    // of this one
-    wait_vm_all();
+    // The next step reads tile pre and its stats, both issued at the top
+    // of this one.  The dS stores issued after them need no wait (nothing
+    // here reads them back), and vector memory operations complete in
+    // issue order, so the wait leaves this step's stores in flight.
+    if constexpr (DS) {
+      if (live && MASKED && ut.tile == 0) wait_vm<8>();
+      else if (live) wait_vm<4>();
+      else wait_vm_all();
+    } else {
+      wait_vm_all();
+    }
     if (pre_live) stage_stats(1 - buf);
     __syncthreads();
     return pre;

@@ -102,29 +102,38 @@ struct TileLoader {
   static constexpr int CHUNKS = ROWS * T::CPR;
   static constexpr int IPW = CHUNKS / (64 * NWAVES);
   static_assert(CHUNKS % (64 * NWAVES) == 0, "tile must split into waves");
-  int row[IPW];     // tile row filled by this lane in instruction i
-  int coff[IPW];    // element offset of its logical chunk within the row
-  int ldsb[IPW];    // wave's LDS byte offset of instruction i (uniform)
-  unsigned boff[IPW];  // byte offset of that chunk from the tile's first
-                       // row when rows are rs elements apart (see init_rs)
+  int w, lane;         // this lane's wave and lane
+  unsigned boff[IPW];  // byte offset of its chunk of instruction i from the
+                       // tile's first row when rows are rs elements apart
+                       // (see init_rs)
 
-  __device__ void init(int w, int lane) {
+  // tile row filled by this lane in instruction i, and the element offset
+  // of its logical chunk within the row
+  __device__ void chunk(int i, int &r, int &co) const {
+    const int c = (w * IPW + i) * 64 + lane;
+    r = c / T::CPR;
+    co = ((c % T::CPR) ^ T::swz(r)) * 8;
+  }
+  // wave's LDS byte offset of instruction i (uniform)
+  __device__ static constexpr int ldsb(int w, int i) {
+    return (w * IPW + i) * 64 * 16;
+  }
+
+  __device__ void init(int w_, int lane_) {
+    w = w_;
+    lane = lane_;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int c = (w * IPW + i) * 64 + lane;
-      const int r = c / T::CPR, pc = c % T::CPR;
-      row[i] = r;
-      coff[i] = (pc ^ T::swz(r)) * 8;
-      ldsb[i] = (w * IPW + i) * 64 * 16;
-      boff[i] = 0;
-    }
+    for (int i = 0; i < IPW; ++i) boff[i] = 0;
   }
   // Precompute the byte offsets used by fast_s(): row < ROWS <= 128 and
   // rs = H*D, so they fit in 32 bits while H*D stays below 2^24.
   __device__ void init_rs(size_t rs) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      boff[i] = (unsigned)(row[i] * rs + coff[i]) * 2u;
+    for (int i = 0; i < IPW; ++i) {
+      int r, co;
+      chunk(i, r, co);
+      boff[i] = (unsigned)(r * rs + co) * 2u;
+    }
   }
 
   // Rows are slots s0 + row of a group, all valid and contiguous from the
@@ -133,7 +142,7 @@ struct TileLoader {
   // addresses stay live across a loop.
   __device__ void fast_s(const bf16_t *g0, char *lds) const {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) g2lds16_s(g0, boff[i], lds + ldsb[i]);
+    for (int i = 0; i < IPW; ++i) g2lds16_s(g0, boff[i], lds + ldsb(w, i));
   }
 
   // General rows: slot s0 + row of the group (run, glen); rows outside
@@ -145,9 +154,10 @@ struct TileLoader {
                           int lo = INT_MIN) const {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
+      int r, co;
+      chunk(i, r, co);
       // opaque copies keep the compiler from hoisting per-lane 64-bit
       // addresses of this (rare) path out of the caller's loop
-      int r = row[i], co = coff[i];
       asm volatile("" : "+v"(r), "+v"(co));
       const int s = s0 + r;
       int pos = 0;
@@ -155,7 +165,7 @@ struct TileLoader {
         pos = run.pos(s);
         if (pos >= L || pos < lo) pos = 0;
       }
-      g2lds16(gbh + (size_t)pos * rs + co, lds + ldsb[i]);
+      g2lds16(gbh + (size_t)pos * rs + co, lds + ldsb(w, i));
     }
   }
 };
@@ -183,6 +193,7 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) |
                              (15 << 8));
 }
+
 
 // ---------------------------------------------------------------------------
 // Document-mask tile lists.  A kernel that walks the 64-slot tiles
