@@ -118,6 +118,26 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       const int *doc_ids, float scale, void *stream);
 
 /*
+ * The backward without any workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, checks and
+ * results as s2attn_bwd, bit for bit, minus delta_ws: delta lives in a
+ * static device array of the library (one per GPU, held until the process
+ * ends) of S2A_NOALLOC_MAX_ROWS floats, so B*H*N must not exceed
+ * S2A_NOALLOC_MAX_ROWS (else S2A_EINVAL, nothing enqueued).  Calls no
+ * allocating routine.  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (on different streams) race and must be ordered
+ * by the caller.
+ */
+#define S2A_NOALLOC_MAX_ROWS (1 << 22) /* 16 MiB of float */
+s2a_status s2attn_bwd_noalloc(const void *q, const void *k, const void *v,
+                              const void *o, int o_dtype, const float *lse,
+                              const void *dout, float *dq, float *dk,
+                              float *dv, int B, int N, int H, int D, int G,
+                              int shift, int boundary, int valid_len,
+                              const int *doc_ids, float scale, void *stream);
+
+/*
  * The three stages of s2attn_bwd, for callers that schedule or time them
  * separately.  Calling them in this order on one stream equals s2attn_bwd;
  * the last two only read delta_ws and may run in either order or

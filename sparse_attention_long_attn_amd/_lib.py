@@ -12,6 +12,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libs2attn.so")
 
+# rows (B*H*N) of the delta array s2attn_bwd_noalloc keeps on the device
+S2A_NOALLOC_MAX_ROWS = 1 << 22
+
 S2A_OK, S2A_EINVAL, S2A_EUNSUPPORTED, S2A_EHIP = 0, 1, 2, 3
 S2A_WRAP, S2A_SPLIT, S2A_CYCLIC = 0, 1, 2
 S2A_BF16, S2A_F32 = 0, 1
@@ -22,7 +25,7 @@ EXPORTS = ("s2attn_fwd", "s2attn_bwd", "s2attn_bwd_preprocess",
            "s2attn_rope", "s2attn_rope_bwd", "s2attn_shard_halo",
            "s2attn_fwd_shard", "s2attn_bwd_shard",
            "s2attn_bwd_ds_workspace", "s2attn_bwd_ds", "s2attn_bwd_dkdv_ds",
-           "s2attn_bwd_dq_ds",
+           "s2attn_bwd_dq_ds", "s2attn_bwd_noalloc",
            "s2attn_strerror", "s2attn_last_error", "s2attn_version")
 
 _lib = None
@@ -50,6 +53,9 @@ def load() -> ctypes.CDLL:
     lib.s2attn_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, P,
                                I, I, I, I, I, I, I, I, P, F, P]
     lib.s2attn_bwd.restype = I
+    lib.s2attn_bwd_noalloc.argtypes = [P, P, P, P, I, P, P, P, P, P,
+                                       I, I, I, I, I, I, I, I, P, F, P]
+    lib.s2attn_bwd_noalloc.restype = I
     lib.s2attn_bwd_preprocess.argtypes = [P, I, P, P, I, I, I, I, P]
     lib.s2attn_bwd_preprocess.restype = I
     lib.s2attn_bwd_dkdv.argtypes = [P, P, P, P, P, P, P, P,

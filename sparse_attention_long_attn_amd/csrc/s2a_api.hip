@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "s2attn.h"
 #include "s2a_device.h"
@@ -183,6 +184,71 @@ s2a_status s2attn_fwd(const void *q, const void *k, const void *v, void *o,
                     "forward launch");
 }
 
+namespace {
+
+// Everything s2attn_bwd and s2attn_bwd_noalloc check before launching; the
+// delta workspace is checked by the caller.
+s2a_status check_bwd(const void *q, const void *k, const void *v,
+                     const void *o, int o_dtype, const float *lse,
+                     const void *dout, float *dq, float *dk, float *dv, int B,
+                     int N, int H, int D, int G, int shift, int boundary,
+                     int valid_len, const int *doc_ids, float scale) {
+  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  if (st != S2A_OK) return st;
+  if (!aligned4(doc_ids))
+    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
+    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(S2A_EINVAL, "scale must be positive and finite");
+  return S2A_OK;
+}
+
+// The delta workspace of s2attn_bwd_noalloc: a device array of the library
+// (one copy per GPU, held until the process ends), never allocated at run
+// time.  Host code uses it only through the per-device address that
+// hipGetSymbolAddress returns; the name itself is not a device address.
+constexpr size_t NOALLOC_DELTA_FLOATS = (size_t)S2A_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[NOALLOC_DELTA_FLOATS];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[MAX_DEVICES];  // address of scratch on each device
+
+// Address of scratch on the current device, looked up on the first call on
+// that device (with it current) and kept.
+s2a_status scratch_of_current_device(float **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    snprintf(g_err, sizeof g_err, "hipGetDevice: %s", hipGetErrorString(e));
+    return S2A_EHIP;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(S2A_EUNSUPPORTED, "device %lld: at most %lld devices", dev,
+                MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      snprintf(g_err, sizeof g_err, "hipGetSymbolAddress(scratch): %s",
+               hipGetErrorString(e));
+      return S2A_EHIP;
+    }
+    g_scratch[dev] = (float *)ptr;
+  }
+  *out = g_scratch[dev];
+  return S2A_OK;
+}
+
+}  // namespace
+
 s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       const void *o, int o_dtype, const float *lse,
                       const void *dout, float *dq, float *dk, float *dv,
@@ -190,25 +256,47 @@ s2a_status s2attn_bwd(const void *q, const void *k, const void *v,
                       int shift, int boundary, int valid_len,
                       const int *doc_ids, float scale, void *stream) {
   g_err[0] = 0;
-  s2a_status st = check_shape(B, N, H, D, G, shift, boundary, valid_len);
+  s2a_status st = check_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, B, N,
+                            H, D, G, shift, boundary, valid_len, doc_ids,
+                            scale);
   if (st != S2A_OK) return st;
-  if (!aligned4(doc_ids))
-    return fail(S2A_EINVAL, "doc_ids must be 4-byte aligned");
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta_ws)
-    return fail(S2A_EINVAL, "NULL tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(delta_ws))
+  if (!delta_ws) return fail(S2A_EINVAL, "NULL tensor pointer");
+  if (!aligned16(delta_ws))
     return fail(S2A_EINVAL, "tensor pointers must be 16-byte aligned");
-  if (o_dtype != S2A_BF16 && o_dtype != S2A_F32)
-    return fail(S2A_EINVAL, "o_dtype=%lld is neither BF16 nor F32", o_dtype);
-  if (!(scale > 0.f) || !isfinite(scale))
-    return fail(S2A_EINVAL, "scale must be positive and finite");
   const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
                                   scale, 1, doc_ids);
   return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
                                    dq, dk, dv, delta_ws, D, p,
                                    (hipStream_t)stream),
+                    "backward launch");
+}
+
+s2a_status s2attn_bwd_noalloc(const void *q, const void *k, const void *v,
+                              const void *o, int o_dtype, const float *lse,
+                              const void *dout, float *dq, float *dk,
+                              float *dv, int B, int N, int H, int D, int G,
+                              int shift, int boundary, int valid_len,
+                              const int *doc_ids, float scale, void *stream) {
+  g_err[0] = 0;
+  s2a_status st = check_bwd(q, k, v, o, o_dtype, lse, dout, dq, dk, dv, B, N,
+                            H, D, G, shift, boundary, valid_len, doc_ids,
+                            scale);
+  if (st != S2A_OK) return st;
+  const long long rows = (long long)B * H * N;
+  if (rows > (long long)NOALLOC_DELTA_FLOATS)
+    return fail(S2A_EINVAL,
+                "B*H*N=%lld rows exceed the %lld of the no-allocation "
+                "workspace (use s2attn_bwd with a workspace)",
+                rows, (long long)NOALLOC_DELTA_FLOATS);
+  float *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != S2A_OK) return st;
+  // The preprocess kernel writes all B*H*N entries of delta before the
+  // gradient kernels read any, so nothing needs clearing.
+  const S2AParams p = make_params(B, N, H, G, shift, boundary, valid_len,
+                                  scale, 1, doc_ids);
+  return hip_status(s2a_launch_bwd(q, k, v, o, o_dtype == S2A_F32, lse, dout,
+                                   dq, dk, dv, ws, D, p, (hipStream_t)stream),
                     "backward launch");
 }
 

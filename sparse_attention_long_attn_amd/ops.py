@@ -104,9 +104,10 @@ def fwd(q, k, v, *, G: int, shift: int | None = None, boundary="wrap",
     return o, lse
 
 
-def _bwd_tensors(q, o, lse, dq, dk, dv, delta):
+def _bwd_tensors(q, o, lse, dq, dk, dv, delta, with_delta=True):
     """Check the forward's outputs and the backward's outputs and Δ
-    workspace (allocated when None) against q's shape and device."""
+    workspace (allocated when None; none with with_delta=False) against
+    q's shape and device."""
     B, N, H, D = q.shape
     f32, dev = torch.float32, q.device
     _need(o, q.shape, (f32, torch.bfloat16), dev, "o")
@@ -115,6 +116,8 @@ def _bwd_tensors(q, o, lse, dq, dk, dv, delta):
     dq = _need(mk() if dq is None else dq, q.shape, f32, dev, "dq")
     dk = _need(mk() if dk is None else dk, q.shape, f32, dev, "dk")
     dv = _need(mk() if dv is None else dv, q.shape, f32, dev, "dv")
+    if not with_delta:
+        return dq, dk, dv, None
     if delta is None:
         delta = torch.empty((B, H, N), dtype=f32, device=dev)
     _need(delta, (B, H, N), f32, dev, "delta")
@@ -139,6 +142,29 @@ def bwd(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
                               _ptr(dv), _ptr(delta), B, N, H, D, G, shift,
                               _boundary(boundary), valid_len,
                               _docs(doc_ids, q), scale, _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, *, G: int, shift: int | None = None,
+                boundary="wrap", valid_len: int | None = None,
+                scale: float | None = None, dq=None, dk=None, dv=None,
+                doc_ids=None):
+    """bwd() without a delta workspace: the library keeps delta in a static
+    device array (B*H*N <= S2A_NOALLOC_MAX_ROWS), so with dq, dk and dv
+    given nothing is allocated.  Calls that overlap on one GPU race.
+    Returns (dq, dk, dv), float32 [B,N,H,D]."""
+    B, N, H, D = _check_qkv(q, k, v, dout)
+    shift = G // 2 if shift is None else shift
+    valid_len = N if valid_len is None else valid_len
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq, dk, dv, _ = _bwd_tensors(q, o, lse, dq, dk, dv, None,
+                                 with_delta=False)
+    odt = _lib.S2A_F32 if o.dtype == torch.float32 else _lib.S2A_BF16
+    _lib.check(_lib.load().s2attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), odt, _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, D, G, shift,
+        _boundary(boundary), valid_len, _docs(doc_ids, q), scale,
+        _stream(q.device)))
     return dq, dk, dv
 
 

@@ -246,3 +246,21 @@ def test_torch_wrappers_reject_host_tensors():
                   "dq")
     with pytest.raises(ValueError, match="ds_ws"):
         ops._ds_arg(ws, torch.device("cuda"))
+
+
+def test_noalloc_backward_rejects_too_many_rows_before_launch():
+    # B*H*N beyond the library's delta array: S2A_EINVAL from the host
+    # checks alone (the pointers below are never dereferenced)
+    lib = _lib.load()
+    fake = 1 << 12                      # aligned, never touched
+    B, N, H, D, G = 1, 1 << 20, 8, 64, 1024
+    assert B * H * N > _lib.S2A_NOALLOC_MAX_ROWS
+    st = lib.s2attn_bwd_noalloc(fake, fake, fake, fake, _lib.S2A_F32, fake,
+                                fake, fake, fake, fake, B, N, H, D, G,
+                                G // 2, _lib.S2A_WRAP, N, None, 0.125, None)
+    assert st == _lib.S2A_EINVAL
+    assert "no-allocation" in lib.s2attn_last_error().decode()
+    # the limit the header states is the one the library enforces
+    hdr = open(os.path.join(ROOT, "include", "s2attn.h")).read()
+    m = re.search(r"#define S2A_NOALLOC_MAX_ROWS \(1 << (\d+)\)", hdr)
+    assert m and (1 << int(m.group(1))) == _lib.S2A_NOALLOC_MAX_ROWS
