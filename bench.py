@@ -60,6 +60,11 @@ def parse():
                     help="time one slice of the headline sequence cut into "
                          "P slices (sequence parallelism, halo exchange "
                          "not included)")
+    ap.add_argument("--config", type=int, default=0, choices=(0, 2, 4, 5),
+                    help="instead of the headline line, time another "
+                         "workload (2: 8K forward, 4: ratio sweep, 5: ragged "
+                         "100K): forward and both backwards, raw and "
+                         "effective throughput, the oracle on a sample")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="time the backward whose dQ kernel recomputes S "
                          "and dP (s2attn_bwd) instead of the one that "
@@ -110,17 +115,49 @@ def load_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def host_info():
+    """Cores this process may run on, the CPU model and the BLAS backend
+    numpy calls (with its thread count)."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = i.get("num_threads")
+                break
+    except Exception:  # pragma: no cover - informational only
+        pass
+    return {"cores": cores, "cpu_model": model, "blas": blas,
+            "blas_threads": threads}
+
+
+def oracle_run(fn, flops, sample):
+    """Time one oracle call; report it as a cpu_baseline record."""
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    info = host_info()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": info["cores"], "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "blas_threads": info["blas_threads"], "sample": sample}
+
+
 def cpu_baseline(cfg):
     """Time the float64 oracle on a bounded sample of the same workload."""
     import numpy as np
     import oracle
     import synthetic as syn
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover - informational only
-        threads = len(os.sched_getaffinity(0))
     B, N, H, D, G = cfg["B"], cfg["N"], cfg["H"], cfg["D"], cfg["G"]
     heads = [0, H // 2]                       # one head of each class
     R = CPU_SAMPLE_ROWS
@@ -129,20 +166,17 @@ def cpu_baseline(cfg):
     x = [syn.bf16_bits_to_f64(ins[t][:, :, heads, :])
          for t in ("q", "k", "v", "do")]
     rows = np.arange(R)
-    t0 = time.perf_counter()
-    oracle.backward(*x, G, G // 2, cfg["boundary"], cfg["L"],
-                    1.0 / D ** 0.5, rows=rows)
-    dt = time.perf_counter() - t0
     # allowed pairs of rows [0, R) in each of the two heads
     pairs = sum(int(oracle.adjacency_block(c, rows, N, G, G // 2,
                                            cfg["boundary"], cfg["L"]).sum())
                 for c in (0, 1))
-    flops = 14 * D * pairs * B
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": dt,
-            "sample": f"float64 oracle fwd+bwd of query rows [0,{R}) of heads "
-                      f"{heads} (one per head class), B={B} N={N} D={D} "
-                      f"G={G} wrap: {pairs} allowed pairs"}
+    return oracle_run(
+        lambda: oracle.backward(*x, G, G // 2, cfg["boundary"], cfg["L"],
+                                1.0 / D ** 0.5, rows=rows),
+        14 * D * pairs * B,
+        f"float64 oracle fwd+bwd of query rows [0,{R}) of heads {heads} "
+        f"(one per head class), B={B} N={N} D={D} G={G} wrap: {pairs} "
+        f"allowed pairs")
 
 
 SWEEP_GS = (12288, 6144, 3072, 2048, 1536)
@@ -216,6 +250,133 @@ def sweep(args):
             }), flush=True)
             del ws
             torch.cuda.empty_cache()
+
+
+# The other workloads (each its own JSON line, never the default):
+#   2  one layer's forward at 8K, G=2048, strict-causal split boundary
+#   4  the group-ratio sweep, B=2 N=12288, every G, split boundary
+#   5  the ragged 100K sequence (valid 100000 of 102400), G=25600, both
+#      boundary variants
+CONFIG_LINES = {
+    2: dict(B=1, N=8192, H=32, D=128, Gs=(2048,), bnds=(1,), L=8192,
+            bwd=False),
+    4: dict(B=2, N=12288, H=32, D=128, Gs=SWEEP_GS, bnds=(1,), L=12288,
+            bwd=True),
+    5: dict(B=1, N=102400, H=32, D=128, Gs=(25600,), bnds=(0, 1), L=100000,
+            bwd=True),
+}
+
+
+def config_bench(args):
+    """Forward (and both backwards) of one other workload, with the raw
+    throughput (pairs counted over the padded length, as if every position
+    were valid) next to the effective one (valid pairs only), and the
+    float64 oracle timed on a stated sample of the same inputs."""
+    import numpy as np
+    import torch
+    import oracle
+    import synthetic as syn
+    import sparse_attention_long_attn_amd as s2a
+    from sparse_attention_long_attn_amd import work
+    c = args.config
+    cfg = CONFIG_LINES[c]
+    B, N, H, D, L = (cfg[k] for k in ("B", "N", "H", "D", "L"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = {syn.WRAP: "wrap", syn.SPLIT: "split", syn.CYCLIC: "cyclic"}
+    for vi, (G, bnd) in enumerate((G, b) for G in cfg["Gs"] for b in cfg["bnds"]):
+        shift = G // 2
+        sc = 1.0 / D ** 0.5
+        ins = syn.make_inputs(c, vi, B, N, H, D, with_do=cfg["bwd"], L=L)
+        t = {k: torch.from_numpy(ins[k].view("int16")).view(torch.bfloat16)
+             .to(dev) for k in ins}
+        kw = dict(G=G, shift=shift, boundary=bnd, valid_len=L, scale=sc)
+        o = torch.empty((B, N, H, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        fwd_ms = timed(lambda: s2a.fwd(t["q"], t["k"], t["v"], o=o, lse=lse,
+                                       **kw))
+        eff = work.total_pairs(B, N, H, G, shift, bnd, L)
+        raw = work.total_pairs(B, N, H, G, shift, bnd, N)
+        line = {"metric": "S2-Attn useful TFLOP/s, other workloads",
+                "config": {"workload": f"config {c}: B={B} N={N} H={H} "
+                                       f"D={D} G={G} shift={shift} "
+                                       f"{names[bnd]} valid_len={L}",
+                           "allowed_pairs_valid": eff,
+                           "allowed_pairs_padded": raw},
+                "steps": args.steps, "warmup": args.warmup,
+                "fwd_ms": round(fwd_ms, 4),
+                "fwd_tflops_effective": round(4 * D * eff / fwd_ms / 1e9, 2),
+                "fwd_tflops_raw": round(4 * D * raw / fwd_ms / 1e9, 2)}
+        if cfg["bwd"]:
+            dq, dk, dv = (torch.empty_like(o) for _ in range(3))
+            delta = torch.empty_like(lse)
+            s2a.fwd(t["q"], t["k"], t["v"], o=o, lse=lse, **kw)
+            ws = s2a.ds_workspace(t["q"], G=G, shift=shift, boundary=bnd)
+            for name, fn in (
+                    ("stored_ds", lambda: s2a.bwd_ds(
+                        t["q"], t["k"], t["v"], o, lse, t["do"], dq=dq,
+                        dk=dk, dv=dv, delta=delta, ds_ws=ws, **kw)),
+                    ("recompute", lambda: s2a.bwd(
+                        t["q"], t["k"], t["v"], o, lse, t["do"], dq=dq,
+                        dk=dk, dv=dv, delta=delta, **kw))):
+                ms = timed(fn)
+                line[f"bwd_{name}_ms"] = round(ms, 4)
+                line[f"step_{name}_ms"] = round(ms + fwd_ms, 4)
+                line[f"step_{name}_tflops_effective"] = round(
+                    14 * D * eff / (ms + fwd_ms) / 1e9, 2)
+                line[f"step_{name}_tflops_raw"] = round(
+                    14 * D * raw / (ms + fwd_ms) / 1e9, 2)
+            line["ds_workspace_bytes"] = ws.numel()
+            del ws
+        # the oracle on a sample: one head of each class, batch row 0,
+        # over the rows of one whole group per head (all rows when a
+        # forward-only workload is small enough)
+        if not args.no_cpu_baseline:
+            heads = [1, H - 2]
+            x = {k: syn.bf16_bits_to_f64(ins[k][:1, :, heads, :]) for k in ins}
+            pairs, calls = 0, []
+            for hi, h in enumerate(heads):
+                cls = int(h >= H // 2)
+                segs = oracle.segments(N, G, shift, bnd)[cls]
+                rows = (np.arange(N) if not cfg["bwd"]
+                        else np.asarray(segs[len(segs) // 2]))
+                pairs += int(oracle.adjacency_block(cls, rows, N, G, shift,
+                                                    bnd, L).sum())
+                calls.append((hi, rows))
+
+            def run():
+                for hi, rows in calls:
+                    if cfg["bwd"]:
+                        oracle.backward(x["q"], x["k"], x["v"], x["do"], G,
+                                        shift, bnd, L, sc, heads=[hi],
+                                        rows=rows)
+                    else:
+                        oracle.forward(x["q"], x["k"], x["v"], G, shift, bnd,
+                                       L, sc, heads=[hi], rows=rows)
+            per = 14 if cfg["bwd"] else 4
+            line["cpu_baseline"] = oracle_run(
+                run, per * D * pairs,
+                f"float64 oracle {'fwd+bwd' if cfg['bwd'] else 'fwd'} of "
+                f"heads {heads} (one per class), batch row 0, "
+                f"{'the rows of the middle group of each class' if cfg['bwd'] else 'all rows'}"
+                f": {pairs} allowed pairs")
+        print(json.dumps(line), flush=True)
+        del t, ins
+        torch.cuda.empty_cache()
 
 
 def rope_bench(args):
@@ -448,6 +609,9 @@ def main():
         return
     if args.shard:
         shard_bench(args)
+        return
+    if args.config:
+        config_bench(args)
         return
 
     import torch

@@ -490,43 +490,80 @@ def group_map(N: int, G: int, *, shift: int | None = None, boundary="wrap",
     return tuple(outs)
 
 
+BACKWARDS = ("auto", "stored_ds", "recompute")
+
+
+def _backward(q, k, v, o, lse, do, G, shift, boundary, valid_len, scale,
+              doc_ids, which):
+    """The backward the autograd op runs.  "stored_ds" keeps dS in a
+    workspace (2 bytes per allowed pair, allocated through torch's caching
+    allocator) and forms dQ from it; it covers D in {64, 128} without a
+    document mask and is the faster one at every measured workload.
+    "recompute" forms dQ by recomputing S and dP and needs only a B*H*N
+    workspace.  "auto" takes stored_ds where it applies and its workspace
+    can be allocated, else recompute."""
+    D = q.shape[3]
+    stored_ok = D in (64, 128) and doc_ids is None
+    if which == "stored_ds" and not stored_ok:
+        raise ValueError("the stored-dS backward needs D in {64, 128} and no "
+                         "document mask")
+    kw = dict(G=G, shift=shift, boundary=boundary, valid_len=valid_len,
+              scale=scale)
+    if which != "recompute" and stored_ok:
+        try:
+            ws = ds_workspace(q, G=G, shift=shift, boundary=boundary)
+        except torch.cuda.OutOfMemoryError:
+            if which == "stored_ds":
+                raise
+            ws = None
+        if ws is not None:
+            return bwd_ds(q, k, v, o, lse, do, ds_ws=ws, **kw)
+    return bwd(q, k, v, o, lse, do, doc_ids=doc_ids, **kw)
+
+
 class S2AttnFunction(torch.autograd.Function):
     """Autograd wrapper: forward and backward both run in the library.
     With rope (a dict of rope() keywords) q and k are the unrotated
     projections: they are rotated at their global positions first, and the
-    gradients are rotated back."""
+    gradients are rotated back.  backward_kind picks the backward (see
+    _backward)."""
 
     @staticmethod
     def forward(ctx, q, k, v, G, shift, boundary, valid_len, scale,
-                doc_ids=None, rope_cfg=None):
+                doc_ids=None, rope_cfg=None, backward_kind="auto"):
+        if backward_kind not in BACKWARDS:
+            raise ValueError(f"backward must be one of {BACKWARDS}")
         if rope_cfg is not None:
             q = rope(q, **rope_cfg)
             k = rope(k, **rope_cfg)
         o, lse = fwd(q, k, v, G=G, shift=shift, boundary=boundary,
                      valid_len=valid_len, scale=scale, doc_ids=doc_ids)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (G, shift, boundary, valid_len, scale, doc_ids, rope_cfg)
+        ctx.cfg = (G, shift, boundary, valid_len, scale, doc_ids, rope_cfg,
+                   backward_kind)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        G, shift, boundary, valid_len, scale, doc_ids, rope_cfg = ctx.cfg
-        dq, dk, dv = bwd(q, k, v, o, lse,
-                         do.to(torch.bfloat16).contiguous(), G=G,
-                         shift=shift, boundary=boundary, valid_len=valid_len,
-                         scale=scale, doc_ids=doc_ids)
+        (G, shift, boundary, valid_len, scale, doc_ids, rope_cfg,
+         which) = ctx.cfg
+        dq, dk, dv = _backward(q, k, v, o, lse,
+                               do.to(torch.bfloat16).contiguous(), G, shift,
+                               boundary, valid_len, scale, doc_ids, which)
         if rope_cfg is not None:
             rope_bwd(dq, out=dq, **rope_cfg)
             rope_bwd(dk, out=dk, **rope_cfg)
         return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype),
-                None, None, None, None, None, None, None)
+                None, None, None, None, None, None, None, None)
 
 
 def s2_attention(q, k, v, G, shift=None, boundary="wrap", valid_len=None,
-                 scale=None, doc_ids=None, rope_cfg=None):
+                 scale=None, doc_ids=None, rope_cfg=None, backward="auto"):
     """Differentiable S²-Attn (float32 output).  rope_cfg: None, or a dict
     of rope() keywords (base, pos_scale, pos_ids, pairing) to rotate q and
-    k at their global positions inside the op."""
+    k at their global positions inside the op.  backward: "auto" (the
+    stored-dS backward where it applies, see _backward), "stored_ds" or
+    "recompute"."""
     return S2AttnFunction.apply(q, k, v, G, shift, boundary, valid_len, scale,
-                                doc_ids, rope_cfg)
+                                doc_ids, rope_cfg, backward)

@@ -157,16 +157,34 @@ def test_attention_with_rope_end_to_end(case):
     compare("dv", dv.cpu().numpy(), rdv, valid_rows=L)
 
     # the autograd op does exactly this composition (gradients come back in
-    # the inputs' dtype)
+    # the inputs' dtype), with either backward
     qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
     oa = s2a.s2_attention(qa, ka, va, G, boundary=boundary, valid_len=L,
-                          scale=sc, doc_ids=dd, rope_cfg=cfg)
+                          scale=sc, doc_ids=dd, rope_cfg=cfg,
+                          backward="recompute")
     oa.backward(do.float())
     torch.cuda.synchronize()
     assert torch.equal(oa, o)
     assert torch.equal(qa.grad, dq.to(torch.bfloat16))
     assert torch.equal(ka.grad, dk.to(torch.bfloat16))
     assert torch.equal(va.grad, dv.to(torch.bfloat16))
+    # "auto" takes the stored-dS backward when there is no document mask
+    # and D is 64 or 128: dk, dv bit for bit as above, dq from the stored dS
+    if dd is None and D in (64, 128):
+        kw_ds = {n: x for n, x in kw.items() if n != "doc_ids"}
+        dq2, _, _ = s2a.bwd_ds(qr, kr, v, o, lse, do, **kw_ds)
+        s2a.rope_bwd(dq2, out=dq2, **cfg)
+    else:
+        dq2 = dq
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    oa = s2a.s2_attention(qa, ka, va, G, boundary=boundary, valid_len=L,
+                          scale=sc, doc_ids=dd, rope_cfg=cfg)
+    oa.backward(do.float())
+    torch.cuda.synchronize()
+    assert torch.equal(qa.grad, dq2.to(torch.bfloat16))
+    assert torch.equal(ka.grad, dk.to(torch.bfloat16))
+    assert torch.equal(va.grad, dv.to(torch.bfloat16))
+    compare("dq (autograd, auto)", dq2.cpu().numpy(), rdq, valid_rows=L)
 
 
 @pytest.mark.parametrize("boundary", [syn.WRAP, syn.SPLIT, syn.CYCLIC])
