@@ -19,6 +19,8 @@
 // and the epilogue writes O and the natural-log LSE at the rows' original
 // positions (the inverse shift costs nothing: addresses come from
 // the group's S2ARun).
+#include <type_traits>
+
 #include "s2a_device.h"
 #include "s2a_kernels.h"
 #include "s2a_tile.h"
@@ -435,7 +437,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   wait_vm_all();
   __syncthreads();
 
-  for (int buf = 0; it < ntiles; buf ^= 1) {
+  // One walk step on the tile in buffer buf (a compile-time constant: the
+  // loop below alternates two copies, so every LDS address of a step is a
+  // register plus an immediate offset, with no per-step address arithmetic).
+  auto step = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int k0 = it * FWD_BK;
     const int nx = DOC ? next_tile(klive, it + 1, ntiles) : it + 1;
     const bool more = nx < ntiles;
@@ -554,6 +560,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     wait_vm_all();
     __syncthreads();
     it = nx;
+  };
+  while (it < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (it >= ntiles) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   const float lt = wave_sum_x32(l_run);
