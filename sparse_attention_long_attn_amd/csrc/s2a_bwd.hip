@@ -983,6 +983,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   const int kpos = kin ? run.pos(key) : 0;
   const bool kvalid = kin && kpos < L;
   const int kdoc = DOC ? p.doc[(size_t)ut.b * N + kpos] : 0;
+  // wave-uniform: every key of the wave valid (the dS stores then need no
+  // per-lane select)
+  const bool all_kvalid = __all(kvalid);
   // Document IDs the wave's keys span: a query tile whose IDs all lie
   // outside [kdmn, kdmx] shares no document with them and is skipped.
   int kdmn = kvalid ? kdoc : INT_MAX, kdmx = kvalid ? kdoc : INT_MIN;
@@ -1027,10 +1030,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
       }
     }
   };
+  // (a product, not a division: the IEEE quotient's fix-up sequence sat
+  // on every step's path to the barrier)
+  const float neg_rscale = -1.f / p.scale;
   auto stage_stats = [&](int buf) {
     if (tid < BQ) {
       // the initial S and dP accumulators of the row (see the body)
-      lse2s[buf * BQ + tid] = -l2st / p.scale;
+      lse2s[buf * BQ + tid] = l2st * neg_rscale;
       dlts[buf * BQ + tid] = -dlst;
       if (DOC) qdocs[buf * BQ + tid] = qdst;
     }
@@ -1232,9 +1238,19 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int off = h2 * 1024 + 16 * ds_slot(hf, l32, h2);
-          u32x4 val = {0u, 0u, 0u, 0u};
-          if (kvalid) val = __builtin_bit_cast(u32x4, sb[qb][h2]);
-          __builtin_nontemporal_store(val, (u32x4 *)(blk + off));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[qb][h2]),
+                                      (u32x4 *)(blk + off));
+          if (!all_kvalid && !kvalid) {
+            // A padded key's column holds garbage: overwrite it with zeros
+            // (a second store from the same lane lands after the first).
+            // Written as asm so that the compiler cannot fold the two
+            // stores into one with a per-lane select on every step.
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            asm volatile("global_store_dwordx4 %0, %1, off nt"
+                         :
+                         : "v"(blk + off), "v"(z)
+                         : "memory");
+          }
           if (MASKED && ut.tile == 0) {
             char *res = (char *)p.dsws + ds_res_block(ut.u, nkb, tt) * DS_BLOCK + cb;
             const int e0 = 8 * h2;
