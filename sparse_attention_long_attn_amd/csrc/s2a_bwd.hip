@@ -61,8 +61,11 @@ constexpr int HOT_SPAN = 64;
 // in blocks of 64 queries x 128 keys (16 KiB): query tile qt (64 slots of
 // the group) against key block kb (the 128 keys of one dK/dV workgroup).
 // Unit u (a (b, h, group), numbered as the grids number them) owns
-// nkb (nkb + 1) + 2 blocks, nkb = ceil(G / 128): first the blocks with
-// qt >= 2 kb (the others hold only queries that precede every key),
+// nkb (nkb + 1) + 2 blocks, nkb = ceil(len / 128) for its group's length
+// len, and the units' blocks lie back to back in unit order (so the short
+// first and last groups of the shifted class under SPLIT, and a class
+// with one group fewer, take only the room they need): first the blocks
+// with qt >= 2 kb (the others hold only queries that precede every key),
 // kb-major, then two residual blocks, kb = 0 and qt = 0, 1, holding
 // dS - bf16(dS).  Queries in the first 128 slots of a group see at most
 // 128 keys, all of them in key block 0; their dS entries are the largest
@@ -76,16 +79,55 @@ constexpr int HOT_SPAN = 64;
 // 32 a + (key ^ 4 (a + 2 h2)): the dQ kernel's transposing reads then
 // touch every LDS bank once.
 constexpr int DS_BLOCK = 16384;
-__host__ __device__ inline int ds_nkb(int G) { return (G + KV_BK - 1) / KV_BK; }
-__device__ inline size_t ds_unit(int u, int nkb) {
-  return (size_t)u * ((size_t)nkb * (nkb + 1) + 2);
+__host__ __device__ inline int ds_nkb(int len) { return (len + KV_BK - 1) / KV_BK; }
+// blocks owned by a unit whose group has len slots
+__host__ __device__ inline long long ds_unit_blocks(int len) {
+  if (len <= 0) return 0;
+  const long long nkb = ds_nkb(len);
+  return nkb * (nkb + 1) + 2;
 }
-__device__ inline size_t ds_block(int u, int nkb, int kb, int qt) {
+// Blocks of one (b, h) of class cls over its groups 0 .. gi-1.  Only the
+// first and the last group of a class can differ from G (s2a_group).
+__host__ __device__ inline long long ds_class_blocks(const S2AGeom &g,
+                                                     int cls, int gi) {
+  const int ng = s2a_num_groups(g, cls);
+  if (gi > ng) gi = ng;
+  if (gi <= 0) return 0;
+  S2ARun run;
+  int len;
+  s2a_group(g, cls, 0, run, len);
+  long long n = ds_unit_blocks(len);
+  const int mid = (gi < ng ? gi : ng - 1) - 1;  // groups 1 .. mid
+  if (mid > 0) n += (long long)mid * ds_unit_blocks(g.G);
+  if (gi == ng && ng >= 2) {
+    s2a_group(g, cls, ng - 1, run, len);
+    n += ds_unit_blocks(len);
+  }
+  return n;
+}
+// First block of unit u = gi (B H) + b H + h (heads h < H/2: class 0);
+// with u = p.units, the blocks of the whole workspace.
+__host__ __device__ inline long long ds_unit_base(const S2AParams &p, int u) {
+  const int BH = p.B * p.H, H0 = p.H >> 1, H1 = p.H - H0;
+  const int gi = u / BH, bh = u - gi * BH, b = bh / p.H, h = bh - b * p.H;
+  long long n = (long long)p.B * (H0 * ds_class_blocks(p.g, 0, gi) +
+                                  H1 * ds_class_blocks(p.g, 1, gi));
+  S2ARun run;
+  int len;
+  const long long b0 = s2a_group(p.g, 0, gi, run, len) ? ds_unit_blocks(len) : 0;
+  const long long b1 = s2a_group(p.g, 1, gi, run, len) ? ds_unit_blocks(len) : 0;
+  n += (long long)b * (H0 * b0 + H1 * b1);  // batches before b in row gi
+  n += (long long)(h < H0 ? h : H0) * b0 + (long long)(h > H0 ? h - H0 : 0) * b1;
+  return n;
+}
+// block (kb, qt) and residual block tt of the unit whose blocks start at
+// base and whose group has nkb key blocks
+__device__ inline size_t ds_block(size_t base, int nkb, int kb, int qt) {
   // kb (2 nkb - kb + 1) = blocks of the key blocks before kb
-  return ds_unit(u, nkb) + (size_t)kb * (2 * nkb - kb + 1) + (qt - 2 * kb);
+  return base + (size_t)kb * (2 * nkb - kb + 1) + (qt - 2 * kb);
 }
-__device__ inline size_t ds_res_block(int u, int nkb, int tt) {
-  return ds_unit(u, nkb) + (size_t)nkb * (nkb + 1) + tt;
+__device__ inline size_t ds_res_block(size_t base, int nkb, int tt) {
+  return base + (size_t)nkb * (nkb + 1) + tt;
 }
 __device__ inline int ds_slot(int a, int key, int h2) {
   return 32 * a + (key ^ (4 * (a + 2 * h2)));
@@ -986,6 +1028,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   // wave-uniform: every key of the wave valid (the dS stores then need no
   // per-lane select)
   const bool all_kvalid = __all(kvalid);
+  // the unit's dS workspace blocks (DS)
+  const size_t ds_base = DS ? (size_t)ds_unit_base(p, ut.u) : 0;
+  const int ds_nkbu = ds_nkb(glen);
   // Document IDs the wave's keys span: a query tile whose IDs all lie
   // outside [kdmn, kdmx] shares no document with them and is skipped.
   int kdmn = kvalid ? kdoc : INT_MAX, kdmx = kvalid ? kdoc : INT_MIN;
@@ -1231,10 +1276,9 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // dS - bf16(dS).  Nontemporal: dQ reads it back from HBM much later.
     auto store_ds = [&](int qb) {
       if constexpr (DS) {
-        const int nkb = ds_nkb(p.g.G);
         const size_t cb = (size_t)((w * 2 + qb) * 2) * 1024;
         char *blk = (char *)p.dsws +
-                    ds_block(ut.u, nkb, ut.tile, 2 * ut.tile + tt) * DS_BLOCK + cb;
+                    ds_block(ds_base, ds_nkbu, ut.tile, 2 * ut.tile + tt) * DS_BLOCK + cb;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int off = h2 * 1024 + 16 * ds_slot(hf, l32, h2);
@@ -1252,7 +1296,7 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
                          : "memory");
           }
           if (MASKED && ut.tile == 0) {
-            char *res = (char *)p.dsws + ds_res_block(ut.u, nkb, tt) * DS_BLOCK + cb;
+            char *res = (char *)p.dsws + ds_res_block(ds_base, ds_nkbu, tt) * DS_BLOCK + cb;
             const int e0 = 8 * h2;
             const bf16x8 hi = sb[qb][h2];
             const bf16x8 lo = to_bf16x8(
@@ -1427,7 +1471,8 @@ __global__ __launch_bounds__(DSQ_THREADS, 1) void s2a_bwd_dq_ds_kernel(
   const size_t rs = (size_t)p.H * D;
   const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
   const bf16_t *kbh = k + boff;
-  const int nkb = ds_nkb(p.g.G);
+  const int nkb = ds_nkb(glen);
+  const size_t ds_base = (size_t)ds_unit_base(p, ut.u);
   const char *dsw = (const char *)p.dsws;
 
   // compute role: 32-query block wq (query tile 2j + wq/2, block wq%2 of
@@ -1457,8 +1502,8 @@ __global__ __launch_bounds__(DSQ_THREADS, 1) void s2a_bwd_dq_ds_kernel(
       ld.fast_s(kbh + (size_t)run.pos(k0) * rs, kd);
     else
       ld.general(kbh, rs, run, glen, k0, L, kd);
-    const size_t blk = res ? ds_res_block(ut.u, nkb, lq >> 1)
-                           : ds_block(ut.u, nkb, kb, lqt);
+    const size_t blk = res ? ds_res_block(ds_base, nkb, lq >> 1)
+                           : ds_block(ds_base, nkb, kb, lqt);
     const char *src = dsw + blk * DS_BLOCK;
     char *dd = kd + TILEB + lq * QBS;
 #pragma unroll
@@ -1879,8 +1924,7 @@ hipError_t launch_dq_t(const void *q, const void *k, const void *v,
 }  // namespace
 
 long double s2a_ds_workspace_bytes(const S2AParams &p) {
-  const long double nkb = ds_nkb(p.g.G);
-  return (long double)p.units * (nkb * (nkb + 1) + 2) * DS_BLOCK;
+  return (long double)ds_unit_base(p, p.units) * DS_BLOCK;
 }
 
 hipError_t s2a_launch_bwd_pre(const void *o, bool o_f32, const void *dout,

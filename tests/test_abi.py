@@ -91,19 +91,40 @@ def test_misaligned_pointer_rejected():
 
 
 def test_stored_ds_workspace_size():
-    # blocks of 64 queries x 128 keys (16 KiB), nkb (nkb + 1) + 2 per unit
-    # with nkb = ceil(G / 128): the causal blocks plus two residual blocks
-    # of key block 0; units = B * H * (groups of the larger class)
+    # blocks of 64 queries x 128 keys (16 KiB): per (b, h, group),
+    # nkb (nkb + 1) + 2 with nkb = ceil(len / 128) for the group's length
+    # (the causal blocks plus two residual blocks of key block 0).  The
+    # group lengths come from the oracle's segments: under SPLIT the shifted
+    # class has two groups of length G/2 and one group more.
+    import oracle
     lib = _lib.load()
     out = ctypes.c_size_t(0)
-    for (B, N, H, D, G, bnd, groups) in [(1, 32768, 32, 128, 8192, 0, 4),
-                                         (2, 12288, 32, 64, 1536, 1, 9),
-                                         (1, 1024, 2, 128, 1024, 2, 1),
-                                         (1, 192, 2, 128, 96, 0, 2)]:
-        assert lib.s2attn_bwd_ds_workspace(B, N, H, D, G, G // 2, bnd,
-                                           ctypes.byref(out)) == _lib.S2A_OK
-        nkb = -(-G // 128)
-        assert out.value == B * H * groups * (nkb * (nkb + 1) + 2) * 16384
+
+    def blocks(n):
+        nkb = -(-n // 128)
+        return nkb * (nkb + 1) + 2
+
+    for (B, N, H, D, G, bnd) in [(1, 32768, 32, 128, 8192, 0),
+                                 (2, 12288, 32, 64, 1536, 1),
+                                 (1, 102400, 32, 128, 25600, 1),
+                                 (1, 102400, 32, 128, 25600, 2),
+                                 (1, 1024, 2, 128, 1024, 2),
+                                 (1, 192, 2, 128, 96, 0),
+                                 (1, 192, 2, 128, 96, 1),
+                                 (2, 1536, 6, 64, 512, 1)]:
+        for shift in (G // 2, 0):
+            assert lib.s2attn_bwd_ds_workspace(B, N, H, D, G, shift, bnd,
+                                               ctypes.byref(out)) == _lib.S2A_OK
+            segs = oracle.segments(N, G, shift, bnd)
+            want = B * sum(blocks(len(seg)) for h in range(H)
+                           for seg in segs[int(h >= H // 2)])
+            assert out.value == want * 16384, (B, N, H, G, bnd, shift)
+    # SPLIT no longer sizes every unit as a full group: at 100K (G = 25600)
+    # it needs a quarter less than before
+    lib.s2attn_bwd_ds_workspace(1, 102400, 32, 128, 25600, 12800, 1,
+                                ctypes.byref(out))
+    full = 32 * 5 * blocks(25600) * 16384
+    assert out.value < 0.76 * full
     assert lib.s2attn_bwd_ds_workspace(1, 64, 4, 32, 16, 8, 0,
                                        ctypes.byref(out)) == _lib.S2A_EUNSUPPORTED
     assert lib.s2attn_bwd_ds_workspace(1, 64, 4, 64, 16, 8, 0,
