@@ -8,7 +8,7 @@
 // that group up to the diagonal are visited, so the work is proportional
 // to the allowed pairs, not to N^2 (§1.1, last paragraph).
 //
-// Per key tile of 64 keys:
+// Per key tile of 32 keys (D >= 64; 64 keys for D < 64):
 //   S^T = K Q^T           bf16 MFMA 32x32x16, fp32 accumulate; each lane
 //                         owns one query column, so the row max needs a
 //                         single cross-lane exchange (lane l <-> l^32)
@@ -28,7 +28,7 @@
 namespace {
 
 constexpr int FWD_BQ = 128;  // query rows per workgroup, 32 per wave
-constexpr int FWD_BK = 64;   // keys per LDS tile
+constexpr int FWD_BK = 64;   // keys per LDS tile (D < 64) and per document-list tile
 constexpr int FWD_THREADS = FWD_BQ / 32 * 64;
 // two waves per SIMD: 256-thread groups two per CU, 512-thread groups one
 constexpr int FWD_MINBLOCKS = 512 / FWD_THREADS;
@@ -304,17 +304,21 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
 }
 
 // Forward for D in {64, 128}: same math as s2a_fwd_kernel, with K/V tiles
-// in the swizzled unpadded layout of s2a_tile.h filled by direct
-// global -> LDS loads (no staging registers, addresses precomputed).
-template <int D, bool OF32, bool DOC>
-__global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
+// of BK keys in the swizzled unpadded layout of s2a_tile.h filled by
+// direct global -> LDS loads (no staging registers, addresses
+// precomputed).  The tiles are 32 keys: 32 KiB of LDS and 162 VGPRs (no
+// document mask), so three workgroups (three waves per SIMD) share a CU,
+// 4-5 % faster at 32K than 64-key tiles with two.
+template <int D, bool OF32, bool DOC, int BK>
+__global__ __launch_bounds__(FWD_THREADS, BK == 32 && !DOC ? 3 : FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
     float *__restrict__ lse, S2AParams p) {
+  static_assert(BK == 32 || BK == 64, "32- or 64-key tiles");
   using T = SwTile<D>;
-  using LD = TileLoader<D, FWD_BK, FWD_THREADS / 64>;
-  constexpr int KSTEPS = D / 16, DB = D / 32;
-  constexpr int TILEB = FWD_BK * T::ROWB;  // bytes per tile buffer
+  using LD = TileLoader<D, BK, FWD_THREADS / 64>;
+  constexpr int KSTEPS = D / 16, DB = D / 32, NKB = BK / 32;
+  constexpr int TILEB = BK * T::ROWB;  // bytes per tile buffer
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
   __shared__ __attribute__((aligned(16))) int kdoc[2][FWD_BK];  // DOC only
   __shared__ unsigned klive[DOC_WORDS];                          // DOC only
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   ld.init_rs(rs);
   auto issue = [&](int k0, int buf) {
     char *kd = Ks + buf * TILEB, *vd = Vs + buf * TILEB;
-    if (tile_plain(run, glen, k0, FWD_BK, L)) {
+    if (tile_plain(run, glen, k0, BK, L)) {
       const size_t r0 = (size_t)run.pos(k0) * rs;
       ld.fast_s(kbh + r0, kd);
       ld.fast_s(vbh + r0, vd);
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
       ld.general(kbh, rs, run, glen, k0, L, kd);
       ld.general(vbh, rs, run, glen, k0, L, vd);
     }
-    if (DOC && w == 0) {  // document IDs of the tile's 64 keys
+    if (DOC && w == 0) {  // document IDs of 64 keys from the tile's first
       const int ks = k0 + lane;
       g2lds4(p.doc + (size_t)b * N + (ks < glen ? run.pos(ks) : 0),
              &kdoc[buf][0]);
@@ -419,21 +423,32 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   float m_ref = -INFINITY, l_run = 0.f;
 
   const int kend = min(glen, q0 + FWD_BQ);
-  const int ntiles = (kend + FWD_BK - 1) / FWD_BK;
+  const int ntiles = (kend + BK - 1) / BK;
   const int wq_lo = q0 + 32 * w;
   const int wq_hi = wq_lo + 31;
   const float c2 = p.scale_log2;
 
   // Under a document mask the workgroup walks only the key tiles whose IDs
-  // can meet its queries' (the rest would be masked out entirely).
+  // can meet its queries' (the rest would be masked out entirely).  The
+  // lists mark 64-key tiles; a 32-key step is live when its 64-key tile is.
+  const int nt64 = (kend + FWD_BK - 1) / FWD_BK;
   if (DOC) {
     int mn = qdmn, mx = qdmx;
     wg_range<FWD_THREADS / 64>(mn, mx, rng, w, lane);
     doc_tiles<FWD_THREADS / 64>(p.doc + (size_t)b * N, run, glen, L, 0,
-                                ntiles, mn, mx, klive, nullptr, w, lane);
+                                nt64, mn, mx, klive, nullptr, w, lane);
   }
-  int it = DOC ? next_tile(klive, 0, ntiles) : 0;
-  if (it < ntiles) issue(it * FWD_BK, 0);
+  // first walked tile >= i (ntiles if none)
+  auto next_walk = [&](int i) {
+    if constexpr (BK == FWD_BK) {
+      return next_tile(klive, i, ntiles);
+    } else {
+      const int t64 = next_tile(klive, i >> 1, nt64);
+      return t64 == (i >> 1) ? i : min(2 * t64, ntiles);
+    }
+  };
+  int it = DOC ? next_walk(0) : 0;
+  if (it < ntiles) issue(it * BK, 0);
   wait_vm_all();
   __syncthreads();
 
@@ -442,10 +457,10 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
   // register plus an immediate offset, with no per-step address arithmetic).
   auto step = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int k0 = it * FWD_BK;
-    const int nx = DOC ? next_tile(klive, it + 1, ntiles) : it + 1;
+    const int k0 = it * BK;
+    const int nx = DOC ? next_walk(it + 1) : it + 1;
     const bool more = nx < ntiles;
-    if (more) issue(nx * FWD_BK, buf ^ 1);  // lands during this tile's math
+    if (more) issue(nx * BK, buf ^ 1);  // lands during this tile's math
 
     // (docedge: the tile's keys and the wave's queries are not all of one
     // document, so the document mask must be applied)
@@ -453,22 +468,22 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     if (DOC && live) {
       // one key ID per lane; ballots rather than a cross-lane min/max,
       // whose dependent shuffles would stall every tile
-      const int kd = kdoc[buf][lane];
+      const int kd = kdoc[buf][lane & (BK - 1)];
       live = __any(kd >= qdmn && kd <= qdmx);
       docedge = !(qdmn == qdmx && __all(kd == qdmn));
     }
     if (live) {
       const char *Kb = Ks + buf * TILEB;
       const char *Vb = Vs + buf * TILEB;
-      // S^T = K Q^T, 16 MFMAs over (kb, t); each operand read runs PIPE
+      // S^T = K Q^T, NKB * KSTEPS MFMAs over (kb, t); each operand read runs PIPE
       // steps ahead of its MFMA (the fences keep the compiler from waiting
       // on every read right before its use)
-      f32x16 sacc[2];
+      f32x16 sacc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      constexpr int PIPE = 3, NS = 2 * KSTEPS;
+      constexpr int PIPE = 3, NS = NKB * KSTEPS;
       bf16x8 a[NS];
       auto opload = [&](int st) {
         a[st] = *(const bf16x8 *)(Kb + (st / KSTEPS) * 32 * T::ROWB +
@@ -486,11 +501,11 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      const bool edge = docedge || (k0 + FWD_BK - 1 > wq_lo) ||
-                        !tile_plain(run, glen, k0, FWD_BK, L);
+      const bool edge = docedge || (k0 + BK - 1 > wq_lo) ||
+                        !tile_plain(run, glen, k0, BK, L);
       if (edge) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             i32x4 kd = {0, 0, 0, 0};
@@ -508,7 +523,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
 
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = wave_max_x32(mx) * c2;
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e =
@@ -541,7 +556,7 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
       // (3 % faster at 32K; the same around the S cluster gains nothing)
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int ks = 0; ks < FWD_BK / 16; ++ks) {
+      for (int ks = 0; ks < BK / 16; ++ks) {
         const f32x16 &sp = sacc[ks >> 1];
         const int e0 = 8 * (ks & 1);
         const bf16x8 pb = to_bf16x8(sp[e0 + 0], sp[e0 + 1], sp[e0 + 2],
@@ -608,7 +623,7 @@ hipError_t launch_fwd_d(const void *q, const void *k, const void *v, void *o,
   dim3 grid((unsigned)units_pad * (unsigned)p.tiles);
   const void *fn;
   if constexpr (D >= 64)
-    fn = (const void *)s2a_fwd_sw_kernel<D, OF32, DOC>;
+    fn = (const void *)s2a_fwd_sw_kernel<D, OF32, DOC, 32>;
   else
     fn = (const void *)s2a_fwd_kernel<D, OF32, DOC>;
   return hipLaunchKernel(fn, grid, dim3(FWD_THREADS), args, 0, st);
