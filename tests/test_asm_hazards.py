@@ -1,7 +1,7 @@
 """Wait states after the hand-placed MFMAs, checked in the gfx950 assembly.
 
 Some kernels keep long-lived accumulators in AGPRs through MFMAs written as
-inline asm (``mfma32_agpr``, ``mfma_group_agpr``).  The compiler does not
+inline asm (``mfma32_agpr``).  The compiler does not
 know the latency of those instructions, so it cannot insert the wait states
 a later instruction needs before it reads, copies or overwrites such an
 accumulator: a 16-pass 32x32x16 MFMA needs 18 (CDNA3/CDNA4 ISA, "Dependency
