@@ -8,7 +8,8 @@
 // that group up to the diagonal are visited, so the work is proportional
 // to the allowed pairs, not to N^2 (§1.1, last paragraph).
 //
-// Per key tile of 32 keys (D >= 64; 64 keys for D < 64):
+// Per key tile of 32 keys (D >= 64 without a document mask; 64 keys
+// otherwise):
 //   S^T = K Q^T           bf16 MFMA 32x32x16, fp32 accumulate; each lane
 //                         owns one query column, so the row max needs a
 //                         single cross-lane exchange (lane l <-> l^32)
@@ -306,15 +307,19 @@ __global__ __launch_bounds__(FWD_THREADS, FWD_MINBLOCKS) void s2a_fwd_kernel(
 // Forward for D in {64, 128}: same math as s2a_fwd_kernel, with K/V tiles
 // of BK keys in the swizzled unpadded layout of s2a_tile.h filled by
 // direct global -> LDS loads (no staging registers, addresses
-// precomputed).  The tiles are 32 keys: 32 KiB of LDS and 162 VGPRs (no
-// document mask), so three workgroups (three waves per SIMD) share a CU,
-// 4-5 % faster at 32K than 64-key tiles with two.
+// precomputed).  Without a document mask the tiles are 32 keys: 32 KiB of
+// LDS and 162 VGPRs, so three workgroups (three waves per SIMD) share a
+// CU, 4-5 % faster at 32K than 64-key tiles with two.  Under a document
+// mask the tiles are 64 keys, the granularity of the document lists: the
+// mask's registers (177 VGPRs with 32-key tiles) leave two workgroups per
+// CU either way, and there 64-key tiles are 7-14 % faster.
 template <int D, bool OF32, bool DOC, int BK>
-__global__ __launch_bounds__(FWD_THREADS, BK == 32 && !DOC ? 3 : FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
+__global__ __launch_bounds__(FWD_THREADS, BK == 32 ? 3 : FWD_MINBLOCKS) void s2a_fwd_sw_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, void *__restrict__ o,
     float *__restrict__ lse, S2AParams p) {
   static_assert(BK == 32 || BK == 64, "32- or 64-key tiles");
+  static_assert(!DOC || BK == FWD_BK, "document lists mark 64-key tiles");
   using T = SwTile<D>;
   using LD = TileLoader<D, BK, FWD_THREADS / 64>;
   constexpr int KSTEPS = D / 16, DB = D / 32, NKB = BK / 32;
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(FWD_THREADS, BK == 32 && !DOC ? 3 : FWD_MINBLOCKS) 
       ld.general(kbh, rs, run, glen, k0, L, kd);
       ld.general(vbh, rs, run, glen, k0, L, vd);
     }
-    if (DOC && w == 0) {  // document IDs of 64 keys from the tile's first
+    if (DOC && w == 0) {  // the tile's 64 document IDs
       const int ks = k0 + lane;
       g2lds4(p.doc + (size_t)b * N + (ks < glen ? run.pos(ks) : 0),
              &kdoc[buf][0]);
@@ -429,24 +434,15 @@ __global__ __launch_bounds__(FWD_THREADS, BK == 32 && !DOC ? 3 : FWD_MINBLOCKS) 
   const float c2 = p.scale_log2;
 
   // Under a document mask the workgroup walks only the key tiles whose IDs
-  // can meet its queries' (the rest would be masked out entirely).  The
-  // lists mark 64-key tiles; a 32-key step is live when its 64-key tile is.
-  const int nt64 = (kend + FWD_BK - 1) / FWD_BK;
+  // can meet its queries' (the rest would be masked out entirely).
   if (DOC) {
     int mn = qdmn, mx = qdmx;
     wg_range<FWD_THREADS / 64>(mn, mx, rng, w, lane);
     doc_tiles<FWD_THREADS / 64>(p.doc + (size_t)b * N, run, glen, L, 0,
-                                nt64, mn, mx, klive, nullptr, w, lane);
+                                ntiles, mn, mx, klive, nullptr, w, lane);
   }
   // first walked tile >= i (ntiles if none)
-  auto next_walk = [&](int i) {
-    if constexpr (BK == FWD_BK) {
-      return next_tile(klive, i, ntiles);
-    } else {
-      const int t64 = next_tile(klive, i >> 1, nt64);
-      return t64 == (i >> 1) ? i : min(2 * t64, ntiles);
-    }
-  };
+  auto next_walk = [&](int i) { return next_tile(klive, i, ntiles); };
   int it = DOC ? next_walk(0) : 0;
   if (it < ntiles) issue(it * BK, 0);
   wait_vm_all();
@@ -623,7 +619,7 @@ hipError_t launch_fwd_d(const void *q, const void *k, const void *v, void *o,
   dim3 grid((unsigned)units_pad * (unsigned)p.tiles);
   const void *fn;
   if constexpr (D >= 64)
-    fn = (const void *)s2a_fwd_sw_kernel<D, OF32, DOC, 32>;
+    fn = (const void *)s2a_fwd_sw_kernel<D, OF32, DOC, DOC ? FWD_BK : 32>;
   else
     fn = (const void *)s2a_fwd_kernel<D, OF32, DOC>;
   return hipLaunchKernel(fn, grid, dim3(FWD_THREADS), args, 0, st);

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import synthetic as syn
-from gpu_helpers import compare, compare_lse, say, scale_for, to_dev
+from gpu_helpers import (ATOL_MAX, ATOL_MEAN, LSE_TOL, compare, compare_lse,
+                         say, scale_for, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,16 +125,23 @@ def test_documents_special_cases(boundary):
     bits = syn.make_inputs(510, boundary, B, N, H, D, with_do=True, L=L)
     q, k, v, do = (to_dev(bits[t]) for t in ("q", "k", "v", "do"))
     sc = scale_for(D)
-    # one document: the same numbers as no document mask
+    # one document: the numbers of no document mask, within the parity
+    # bounds (the masked forward walks 64-key tiles, the unmasked one
+    # 32-key tiles, so the online softmax rounds P against other running
+    # maxima), and -inf in the same places
     plain = _run(q, k, v, do, G, boundary, L, sc, None)
     one = _run(q, k, v, do, G, boundary, L, sc,
                torch.zeros((B, N), dtype=torch.int32, device="cuda"))
     for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), plain, one):
         fin = torch.isfinite(x)
         assert torch.equal(fin, torch.isfinite(y)), name
-        d = (x[fin] - y[fin]).abs().max().item()
-        say(f"  one document vs none, {name}: max|d|={d:.3e}")
-        assert d <= 1e-6, name
+        d = (x[fin] - y[fin]).abs()
+        say(f"  one document vs none, {name}: max|d|={d.max().item():.3e} "
+            f"mean {d.mean().item():.3e}")
+        if name == "lse":
+            assert d.max().item() <= LSE_TOL, name
+        else:
+            assert d.max().item() <= ATOL_MAX and d.mean().item() <= ATOL_MEAN, name
     # one token per document: o = v, lse = scale q.k, dv = dO and no q/k
     # gradient, up to fp32 rounding (the softmax weight is exp of a
     # rounding residual, and dS = P (dO.v - dO.o) cancels to its rounding)
