@@ -1376,16 +1376,11 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     }
     }  // live
     // The next step reads tile pre and its stats, both issued at the top
-    // of this one.  The dS stores issued after them need no wait (nothing
-    // here reads them back), and vector memory operations complete in
-    // issue order, so the wait leaves this step's stores in flight.
-    if constexpr (DS) {
-      if (live && MASKED && ut.tile == 0) wait_vm<8>();
-      else if (live) wait_vm<4>();
-      else wait_vm_all();
-    } else {
-      wait_vm_all();
-    }
+    // of this one.  The wait covers this step's dS stores too: a partial
+    // count would leave them in flight only if every store retired after
+    // the loads issued before it, an order this code does not rely on for
+    // direct-to-LDS loads and nontemporal stores.
+    wait_vm_all();
     if (pre_live) stage_stats(1 - buf);
     __syncthreads();
     return pre;
