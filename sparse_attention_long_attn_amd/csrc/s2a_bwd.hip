@@ -1273,7 +1273,13 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
     // DS: block qb's dS (bf16, as the dK product takes it) to the tile's
     // workspace block, zero for keys outside the group or padded; in key
     // block 0, on its two masked tiles, also the rounding residual
-    // dS - bf16(dS).  Nontemporal: dQ reads it back from HBM much later.
+    // dS - bf16(dS).  dQ reads it back from HBM much later, so the stores
+    // stream at system scope (sc0 sc1 nt): written through the L2 without
+    // displacing the Q/dO tiles that later steps of the unit read again
+    // (plain nontemporal stores left dK/dV fetching 27 % more from HBM).
+    // Inside asm the compiler does not see a store of more than 8 bytes, so
+    // each one is followed by the two wait states gfx950 requires before
+    // its data registers may be overwritten.
     auto store_ds = [&](int qb) {
       if constexpr (DS) {
         const size_t cb = (size_t)((w * 2 + qb) * 2) * 1024;
@@ -1282,15 +1288,17 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int off = h2 * 1024 + 16 * ds_slot(hf, l32, h2);
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sb[qb][h2]),
-                                      (u32x4 *)(blk + off));
+          asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1"
+                       :
+                       : "v"(blk + off), "v"(__builtin_bit_cast(u32x4, sb[qb][h2]))
+                       : "memory");
           if (!all_kvalid && !kvalid) {
             // A padded key's column holds garbage: overwrite it with zeros
             // (a second store from the same lane lands after the first).
             // Written as asm so that the compiler cannot fold the two
             // stores into one with a per-lane select on every step.
             const u32x4 z = {0u, 0u, 0u, 0u};
-            asm volatile("global_store_dwordx4 %0, %1, off nt"
+            asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1"
                          :
                          : "v"(blk + off), "v"(z)
                          : "memory");
