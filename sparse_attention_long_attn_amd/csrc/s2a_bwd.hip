@@ -1435,8 +1435,10 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
 // through a ring of DSQ_STAGES LDS buffers, DSQ_STAGES - 1 of them in
 // flight: the K tile (swizzled) and the 16 dS chunks of 1 KiB (four per
 // 32-query block), copied unchanged by direct global -> LDS loads spread
-// evenly over the waves.  Transposing reads turn the chunks into the
-// MFMA's B operand (one query per lane, eight keys).  Eight waves, two per
+// evenly over the waves (the dS chunks as streaming loads: read once, they
+// would otherwise push the unit's K tiles out of the L2).  Transposing
+// reads turn the chunks into the MFMA's B operand (one query per lane,
+// eight keys).  Eight waves, two per
 // SIMD: wave w takes the 32 queries of block w % 4 and half of the head
 // width, so one wave's MFMAs run while the other waits on its LDS reads.
 constexpr int DSQ_STAGES = 4;
@@ -1513,7 +1515,7 @@ __global__ __launch_bounds__(DSQ_THREADS, 1) void s2a_bwd_dq_ds_kernel(
     for (int cc = 0; cc < 2; ++cc) {
       // chunk c (wave 2h + c/2 of dK/dV, block lqb, h2 = c%2)
       const int c = 2 * (w & 1) + cc;
-      g2lds16_s(src + (((2 * h + (c >> 1)) * 2 + lqb) * 2 + (c & 1)) * 1024,
+      g2lds16_snt(src + (((2 * h + (c >> 1)) * 2 + lqb) * 2 + (c & 1)) * 1024,
                 lane * 16, dd + c * 1024);
     }
   };

@@ -81,6 +81,24 @@ __device__ __forceinline__ void g2lds16_s(const void *gbase, unsigned off,
                : "memory", "m0");
 }
 
+// The same, streaming (nt): for data read once, so that it does not
+// displace lines that later loads of the kernel read again.
+__device__ __forceinline__ void g2lds16_snt(const void *gbase, unsigned off,
+                                          void *lds_wave) {
+  // (both are wave-uniform; readfirstlane tells the compiler so, which the
+  // scalar operands need)
+  const unsigned m0 =
+      (unsigned)__builtin_amdgcn_readfirstlane((int)(uintptr_t)lds_wave);
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint64_t gu =
+      ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
+      (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)g);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(off), "s"(gu), "s"(m0)
+               : "memory", "m0");
+}
+
 // Direct global -> LDS copy of 4 bytes per lane (lane i lands at byte 4*i
 // past lds_wave, which must be the same for every lane of the wave).  Inline
 // asm for the reason given at g2lds16.
