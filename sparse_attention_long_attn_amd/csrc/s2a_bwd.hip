@@ -1428,6 +1428,431 @@ __global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_sw_kernel(
   }
 }
 
+// dK/dV for D = 128 without a document mask, 64 keys per wave.  Every
+// operand of the Q and dO tiles read from LDS (a row block, or its
+// transpose) feeds the MFMAs of both of the wave's 32-key halves, so the
+// LDS supplies 0.75 KiB per MFMA instead of 1 KiB: V stays in registers,
+// K for the workgroup's 256 keys is read from LDS (a register copy of it
+// would not fit beside the 256 accumulator registers of dK and dV), in
+// phase A, which has no element work to share the step with.
+// The workgroup (4 waves, one per SIMD) owns 256 keys, two key blocks of
+// the dS workspace; wave w's halves are the 32-key chunks 2 (w % 2) and
+// 2 (w % 2) + 1 of key block 2 t + w / 2 (t: the workgroup's tile), so the
+// workspace and the dQ kernel that reads it are those of the 32-key waves.
+// Per 32-query block a wave runs four MFMA phases, the element work of the
+// block overlapping its own later phases:
+//   A  S = Q K^T, both halves             (MFMA; K from LDS)
+//   B  dP = dO V^T                        || P = exp2(c2 S), packed (VALU)
+//   C  dV^T += dO^T P                     || dS = P dP, packed, stored
+//   D  dK^T += Q^T dS
+constexpr int W64_BK = 256;  // keys per workgroup of the 64-key-wave kernel
+
+template <bool DS>
+__global__ __launch_bounds__(THREADS, 1) void s2a_bwd_dkdv_w64_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+    const bf16_t *__restrict__ v, const bf16_t *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ delta,
+    float *__restrict__ dk, float *__restrict__ dv, S2AParams p) {
+  constexpr int D = 128, BQ = 64;
+  using T = SwTile<D>;
+  using LD = TileLoader<D, BQ, THREADS / 64>;
+  using LDV = TileLoader<D, W64_BK, THREADS / 64>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  constexpr int TILEB = BQ * T::ROWB;
+  __shared__ __attribute__((aligned(1024))) char Qs0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Qs1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char dOs0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char dOs1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Ks[W64_BK * T::ROWB];
+  __shared__ __attribute__((aligned(16))) float lse2s[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float dlts[2 * BQ];
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  auto qbuf = [&](auto b) -> char * {
+    if constexpr (decltype(b)::value == 0) return Qs0;
+    else return Qs1;
+  };
+  auto gbuf = [&](auto b) -> char * {
+    if constexpr (decltype(b)::value == 0) return dOs0;
+    else return dOs1;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane >> 4;
+  const int trow = 4 * hf + ((lane & 15) >> 2);
+
+  const UnitTile ut = decode(p, false);
+  if (!ut.ok) return;
+  const S2ARun run = ut.run;
+  const int glen = ut.glen;
+  const int k0 = ut.tile * W64_BK;
+  if (k0 >= glen) return;
+  const int N = p.g.N, L = p.g.L;
+  const size_t rs = (size_t)p.H * D;
+  const size_t boff = (size_t)ut.b * N * rs + (size_t)ut.h * D;
+  const size_t lrow = ((size_t)ut.b * p.H + ut.h) * N;
+  const bf16_t *qbh = q + boff, *gbh = dout + boff;
+  const float c2 = p.scale_log2;
+
+  const int kw0 = k0 + 64 * w;  // the wave's first key
+  int kpos[2];
+  bool kin[2], kvalid[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int key = kw0 + 32 * kh + l32;
+    kin[kh] = key < glen;
+    kpos[kh] = kin[kh] ? run.pos(key) : 0;
+    kvalid[kh] = kin[kh] && kpos[kh] < L;
+  }
+  // wave-uniform: every key of the wave valid (the dS stores then need no
+  // per-lane select)
+  const bool all_kvalid = __all(kvalid[0] && kvalid[1]);
+  // the wave's key block of the dS workspace and its chunks there
+  const int kb = 2 * ut.tile + (w >> 1);
+  const int wv0 = 2 * (w & 1);
+  const size_t ds_base = DS ? (size_t)ds_unit_base(p, ut.u) : 0;
+  const int ds_nkbu = ds_nkb(glen);
+
+  bf16x8 vreg[2][KSTEPS];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const size_t off = boff + (size_t)kpos[kh] * rs;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (kvalid[kh]) a = *(const u32x4 *)(v + off + 16 * t + 8 * hf);
+      vreg[kh][t] = __builtin_bit_cast(bf16x8, a);
+    }
+  }
+
+  LD ld;
+  ld.init(w, lane);
+  ld.init_rs(rs);
+  // K of the workgroup's 256 keys, once (keys outside the group or padded
+  // read position 0: finite data whose products stay in their own columns)
+  {
+    LDV lk;
+    lk.init(w, lane);
+    lk.init_rs(rs);
+    const bf16_t *kbh = k + boff;
+    if (tile_plain(run, glen, k0, W64_BK, L))
+      lk.fast_s(kbh + (size_t)run.pos(k0) * rs, Ks);
+    else
+      lk.general(kbh, rs, run, glen, k0, L, Ks);
+  }
+  // Per-row statistics of a query tile (see s2a_bwd_dkdv_sw_kernel).
+  float l2st = INFINITY, dlst = 0.f;
+  auto fetch_stats = [&](int q0) {
+    if (tid < BQ) {
+      const int qsl = q0 + tid;
+      l2st = INFINITY;
+      dlst = 0.f;
+      if (qsl < glen) {
+        const int qp = run.pos(qsl);
+        if (qp < L && qp >= 0) {
+          l2st = lse[lrow + qp];
+          dlst = delta[lrow + qp];
+        }
+      }
+    }
+  };
+  const float neg_rscale = -1.f / p.scale;
+  auto stage_stats = [&](int buf) {
+    if (tid < BQ) {
+      lse2s[buf * BQ + tid] = l2st * neg_rscale;
+      dlts[buf * BQ + tid] = -dlst;
+    }
+  };
+  auto issue_tile = [&](int q0, auto b) {
+    char *qd = qbuf(b), *gd = gbuf(b);
+    if (tile_plain(run, glen, q0, BQ, L, 0)) {
+      const size_t r0 = (size_t)run.pos(q0) * rs;
+      ld.fast_s(qbh + r0, qd);
+      ld.fast_s(gbh + r0, gd);
+    } else {
+      ld.general(qbh, rs, run, glen, q0, L, qd, 0);
+      ld.general(gbh, rs, run, glen, q0, L, gd, 0);
+    }
+  };
+  // Operand offsets of step t / d-block db.  At D = 128 a row is one
+  // 256-byte sweep and the step's chunk bits enter only by XOR
+  // (T::off(r, c) = 256 r + ((c ^ swz(r)) << 4), 2t and 4db above the
+  // lane's own chunk bits), so one register per read kind serves all steps:
+  //   aoff(t) = aoff0 ^ (t << 5),  troff(db) = troff0 ^ (db << 6).
+  static_assert(T::ROWB == 256, "one row per LDS sweep");
+  const int aoff0 = T::off(l32, hf);
+  const int c0 = 2 * (grp & 1) + ((lane & 3) >> 1);
+  const int troff0 = T::off(trow, c0) + (lane & 1) * 8;
+  const int troff80 = T::off(trow + 8, c0) + (lane & 1) * 8;
+  auto aoff = [&](int t) { return aoff0 ^ (t << 5); };
+
+  f32x16 dkacc[2][DB], dvacc[2][DB];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dkacc[kh][db][i] = 0.f;
+        dvacc[kh][db][i] = 0.f;
+      }
+
+  const int nq = (glen - k0 + BQ - 1) / BQ;
+  // The walk: query tiles 0 .. 3 (the ones that can precede some of the
+  // keys) run the masked body, later tiles the plain one; in a shard the
+  // tiles before the first query of the slice hold halo rows only.
+  constexpr int NMASK = W64_BK / BQ;
+  const int fq = s2a_first_query_slot(run, glen);
+  const int skip = max(0, (fq - k0) / BQ - NMASK);
+  auto next_walk = [&](int t) {
+    int n = t + 1;
+    if (n == NMASK) n += skip;
+    return n;
+  };
+  fetch_stats(k0);
+  wait_vm_all();
+  stage_stats(0);
+  issue_tile(k0, B0{});
+  wait_vm_all();
+  __syncthreads();
+
+  bf16x8 sb[2][2];  // dS of the block in progress, packed (also stored)
+  auto body = [&](auto masked_tag, auto b, int tt) -> int {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int buf = decltype(b)::value;
+    using BN = std::integral_constant<int, 1 - buf>;
+    const int q0 = k0 + tt * BQ;
+    const int qt = q0 / BQ;  // (k0 is a multiple of 256)
+    const int pre = next_walk(tt);
+    const bool pre_live = pre < nq;
+    if (pre_live) {
+      fetch_stats(k0 + pre * BQ);
+      issue_tile(k0 + pre * BQ, BN{});
+    }
+    const char *Qb = qbuf(b);
+    const char *dOb = gbuf(b);
+    const float *l2b = lse2s + buf * BQ;
+    const float *dlb = dlts + buf * BQ;
+    const char *Kw = Ks + 64 * w * T::ROWB;
+    // A wave computes the tiles whose workspace block (kb, qt) exists:
+    // waves 2 and 3 skip the two tiles whose queries all precede their
+    // keys, and a wave whose key block lies past the group's skips all.
+    // The masked tiles yield zeros, stored as such, and so do keys past the
+    // group's end or padded (the dQ kernel reads whole blocks).
+    if (qt >= 2 * kb && kb < ds_nkbu) {
+      constexpr int PIPE = 2;  // operand steps loaded ahead
+      // operand step n (0 .. 63) of the tile: block n / 32, phase
+      // (n / 8) % 4, step n % 8; phase A steps also read two K operands,
+      // one step ahead (registers are short)
+      bf16x8 op[PIPE + 1], ko[2][2];
+      auto kload = [&](int n) {
+        const int s = n & 7;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          ko[n & 1][kh] = *(const bf16x8 *)(Kw + kh * 32 * T::ROWB + aoff(s));
+      };
+      auto opload = [&](int n) {
+        const int qb = n >> 5, ph = (n >> 3) & 3, s = n & 7;
+        bf16x8 &o = op[n % (PIPE + 1)];
+        if (ph == 0) {
+          o = *(const bf16x8 *)(Qb + qb * 32 * T::ROWB + aoff(s));
+        } else if (ph == 1) {
+          o = *(const bf16x8 *)(dOb + qb * 32 * T::ROWB + aoff(s));
+        } else {
+          const int h2 = s / DB, db = s % DB;
+          const char *r = (ph == 2 ? dOb : Qb) + (qb * 32 + 16 * h2) * T::ROWB;
+          o = cat4(lds_read_tr((const bf16_t *)(r + (troff0 ^ (db << 6)))),
+                   lds_read_tr((const bf16_t *)(r + (troff80 ^ (db << 6)))));
+        }
+      };
+      f32x16 S[2], dP[2];
+      bf16x8 pb[2][2];
+      // element e (0 .. 31) of a block: half kh = (e / 8) % 2, C element
+      // i = 8 (e / 16) + e % 8 (query 8 (i / 4) + 4 hf + i % 4 of the block)
+      auto elem_p = [&](int qb, int e) {
+        const int kh = (e >> 3) & 1, i = 8 * (e >> 4) + (e & 7);
+        float pp = __builtin_amdgcn_exp2f(S[kh][i] * c2);
+        if (MASKED) {
+          const int d0 = q0 + 32 * qb + 4 * hf - (kw0 + 32 * kh + l32);
+          if (d0 + 8 * (i >> 2) + (i & 3) < 0) pp = 0.f;
+        }
+        S[kh][i] = pp;
+        if ((e & 7) == 7) {
+          const int e0 = 8 * (e >> 4);
+          pb[kh][e >> 4] = to_bf16x8(S[kh][e0], S[kh][e0 + 1], S[kh][e0 + 2], S[kh][e0 + 3],
+                                     S[kh][e0 + 4], S[kh][e0 + 5], S[kh][e0 + 6], S[kh][e0 + 7]);
+        }
+      };
+      auto store_chunk = [&](int qb, int kh, int h2) {
+        if constexpr (DS) {
+          char *blk = (char *)p.dsws + ds_block(ds_base, ds_nkbu, kb, qt) * DS_BLOCK +
+                      (size_t)(((wv0 + kh) * 2 + qb) * 2) * 1024;
+          const int off = h2 * 1024 + 16 * ds_slot(hf, l32, h2);
+          asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1"
+                       :
+                       : "v"(blk + off), "v"(__builtin_bit_cast(u32x4, sb[kh][h2]))
+                       : "memory");
+          if (!all_kvalid && !kvalid[kh]) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1"
+                         :
+                         : "v"(blk + off), "v"(z)
+                         : "memory");
+          }
+          if (MASKED && kb == 0 && qt < 2) {
+            // rows in the first 128 slots of the group: the rounding
+            // residual dS - bf16(dS) to the residual block of their tile
+            char *res = (char *)p.dsws + ds_res_block(ds_base, ds_nkbu, qt) * DS_BLOCK +
+                        (size_t)(((wv0 + kh) * 2 + qb) * 2) * 1024;
+            const int e0 = 8 * h2;
+            const bf16x8 hi = sb[kh][h2];
+            const bf16x8 lo = to_bf16x8(
+                dP[kh][e0] - (float)hi[0], dP[kh][e0 + 1] - (float)hi[1],
+                dP[kh][e0 + 2] - (float)hi[2], dP[kh][e0 + 3] - (float)hi[3],
+                dP[kh][e0 + 4] - (float)hi[4], dP[kh][e0 + 5] - (float)hi[5],
+                dP[kh][e0 + 6] - (float)hi[6], dP[kh][e0 + 7] - (float)hi[7]);
+            u32x4 rv = {0u, 0u, 0u, 0u};
+            if (kvalid[kh]) rv = __builtin_bit_cast(u32x4, lo);
+            __builtin_nontemporal_store(rv, (u32x4 *)(res + off));
+          }
+        }
+      };
+      auto elem_ds = [&](int qb, int e) {
+        const int kh = (e >> 3) & 1, i = 8 * (e >> 4) + (e & 7);
+        dP[kh][i] = S[kh][i] * dP[kh][i];
+        if ((e & 7) == 7) {
+          const int h2 = e >> 4, e0 = 8 * h2;
+          sb[kh][h2] = to_bf16x8(dP[kh][e0], dP[kh][e0 + 1], dP[kh][e0 + 2], dP[kh][e0 + 3],
+                                 dP[kh][e0 + 4], dP[kh][e0 + 5], dP[kh][e0 + 6], dP[kh][e0 + 7]);
+          store_chunk(qb, kh, h2);
+        }
+      };
+      // one 32-query block: four phases of eight steps; step t of phase ph
+      // uses operand step n = 32 qb + 8 ph + t, loaded PIPE steps ahead
+      auto block = [&](auto qbc) {
+        constexpr int qb = decltype(qbc)::value;
+        // the row statistics enter as the accumulators' initial values
+        // (see s2a_bwd_dkdv_sw_kernel)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 a = *(const f32x4 *)(l2b + 32 * qb + 8 * i4 + 4 * hf);
+          const f32x4 d = *(const f32x4 *)(dlb + 32 * qb + 8 * i4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S[0][4 * i4 + e] = a[e];
+            S[1][4 * i4 + e] = a[e];
+            dP[0][4 * i4 + e] = d[e];
+            dP[1][4 * i4 + e] = d[e];
+          }
+        }
+        if (qb == 0) {
+#pragma unroll
+          for (int n = 0; n < PIPE; ++n) opload(n);
+          kload(0);
+        }
+        auto ahead = [&](int n) {
+          if (n + PIPE < 64) opload(n + PIPE);
+          // (block 1's first K operands during block 0's last step)
+          if (n == 31) kload(32);
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {  // A
+          const int n = 32 * qb + t;
+          ahead(n);
+          if (t < 7) kload(n + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 &o = op[n % (PIPE + 1)];
+          S[0] = mfma32(o, ko[n & 1][0], S[0]);
+          S[1] = mfma32(o, ko[n & 1][1], S[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {  // B
+          const int n = 32 * qb + 8 + t;
+          ahead(n);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 &o = op[n % (PIPE + 1)];
+          dP[0] = mfma32(o, vreg[0][t], dP[0]);
+          dP[1] = mfma32(o, vreg[1][t], dP[1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) elem_p(qb, 4 * t + e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {  // C
+          const int n = 32 * qb + 16 + t;
+          ahead(n);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 &o = op[n % (PIPE + 1)];
+          const int h2 = t / DB, db = t % DB;
+          mfma32_agpr(dvacc[0][db], o, pb[0][h2]);
+          mfma32_agpr(dvacc[1][db], o, pb[1][h2]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) elem_ds(qb, 4 * t + e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {  // D
+          const int n = 32 * qb + 24 + t;
+          ahead(n);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 &o = op[n % (PIPE + 1)];
+          const int h2 = t / DB, db = t % DB;
+          mfma32_agpr(dkacc[0][db], o, sb[0][h2]);
+          mfma32_agpr(dkacc[1][db], o, sb[1][h2]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      block(std::integral_constant<int, 0>{});
+      block(std::integral_constant<int, 1>{});
+    }
+    // (the wait covers the dS stores too, as in s2a_bwd_dkdv_sw_kernel)
+    wait_vm_all();
+    if (pre_live) stage_stats(1 - buf);
+    __syncthreads();
+    return pre;
+  };
+
+  static_assert(NMASK == 4, "four masked steps");
+  int tt = 0;
+  if (tt < nq) tt = body(std::true_type{}, B0{}, tt);
+  if (tt < nq) tt = body(std::true_type{}, B1{}, tt);
+  if (tt < nq) tt = body(std::true_type{}, B0{}, tt);
+  if (tt < nq) tt = body(std::true_type{}, B1{}, tt);
+  while (tt < nq) {
+    tt = body(std::false_type{}, B0{}, tt);
+    if (tt >= nq) break;
+    tt = body(std::false_type{}, B1{}, tt);
+  }
+
+  mfma_agpr_drain();
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    if (kin[kh]) {
+      const size_t row = boff + (size_t)kpos[kh] * rs;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = 32 * db + 8 * i4 + 4 * hf;
+          f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+          if (kvalid[kh]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kk[e] = dkacc[kh][db][4 * i4 + e] * p.scale;
+              vv[e] = dvacc[kh][db][4 * i4 + e];
+            }
+          }
+          *(f32x4 *)(dk + row + d) = kk;
+          *(f32x4 *)(dv + row + d) = vv;
+        }
+    }
+  }
+}
+
 // dQ from the stored dS (D in {64, 128}): dQ^T += K^T dS^T over the key
 // blocks 0 .. j of query tile j (128 queries), and for tile 0 over the
 // residual blocks as well.  Nothing is recomputed, so the kernel
@@ -1856,12 +2281,24 @@ hipError_t launch_dkdv_d(const void *q, const void *k, const void *v,
   void *args[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
                   (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
                   (void *)&p};
-  const void *fn;
-  if constexpr (D >= 64)
-    fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, DOC, DS>;
-  else
-    fn = (const void *)s2a_bwd_dkdv_kernel<D, DOC>;
-  hipError_t e = hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+  hipError_t e;
+  if constexpr (D == 128 && !DOC) {
+    // 64 keys per wave (256 per workgroup)
+    S2AParams pw = p;
+    pw.tiles = (p.g.G + W64_BK - 1) / W64_BK;
+    void *wargs[] = {(void *)&qq,  (void *)&kk,    (void *)&vv, (void *)&gg,
+                     (void *)&lse, (void *)&delta, (void *)&dk, (void *)&dv,
+                     (void *)&pw};
+    e = hipLaunchKernel((const void *)s2a_bwd_dkdv_w64_kernel<DS>,
+                        unit_grid(pw, W64_BK), dim3(THREADS), wargs, 0, st);
+  } else {
+    const void *fn;
+    if constexpr (D >= 64)
+      fn = (const void *)s2a_bwd_dkdv_sw_kernel<D, KV_BQ, DOC, DS>;
+    else
+      fn = (const void *)s2a_bwd_dkdv_kernel<D, DOC>;
+    e = hipLaunchKernel(fn, unit_grid(p, KV_BK), dim3(THREADS), args, 0, st);
+  }
   if constexpr (D >= 64) {
     // the sw kernel rounds P and dS to bf16 everywhere; add the residuals
     // of the hot tiles (the generic kernel does so inline).  Without a
