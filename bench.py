@@ -704,7 +704,7 @@ def main():
     D_pairs = f_fwd // (4 * D)
     kernels = {
         "s2a_fwd_sw_kernel": (fwd_ms, f_fwd),
-        "s2a_bwd_dkdv_sw_kernel": (dkdv_ms, 8 * D * D_pairs),
+        "s2a_bwd_dkdv_w64_kernel": (dkdv_ms, 8 * D * D_pairs),
         ("s2a_bwd_dq_ds_kernel" if stored else "s2a_bwd_dq_sw_kernel"):
             (dq_ms, 2 * D * D_pairs),
     }
