@@ -15,6 +15,10 @@
 //                                                          transposing LDS reads)
 //                        and stores dK, dV once at the end; its DS variant
 //                        also stores bf16 dS to a workspace;
+//   s2a_bwd_dkdv_w64_kernel (D = 128 without a document mask) the same
+//                        work with 64 keys per wave and 256 per workgroup,
+//                        so each Q or dO operand read from LDS feeds two
+//                        MFMAs (it replaces the one above there);
 //   s2a_bwd_dq_kernel / s2a_bwd_dq_sw_kernel
 //                        one workgroup owns 128 queries of one group and
 //                        walks the group's key tiles up to them, in the
